@@ -1,0 +1,79 @@
+"""MI355X (gfx950) chunked prefill of Kimi Delta Attention (KDA).
+
+    o_t = S_t^T q_t,  S_t = (I - beta_t k_t k_t^T) Diag(exp g_t) S_{t-1} + beta_t k_t v_t^T
+
+per (sequence, head), K = V = 128, bf16 or fp32 q/k/v, fp32 g/beta/state, batched
+or variable-length (cu_seqlens), optional initial and final states. The work
+runs in the HIP library libkda.so (include/kda.h); this module only marshals
+torch tensors (device memory and the current stream) into its C ABI.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import torch
+
+from ._lib import KDA_BF16, KDA_F32, Desc, KDAError, lib, status_string  # noqa: F401
+
+__all__ = ["fwd", "KDAError", "status_string", "version"]
+
+D = 128
+
+
+def version() -> int:
+    return int(lib().kda_version())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _desc(q: torch.Tensor, cu_seqlens: Optional[torch.Tensor]) -> Desc:
+    B, T, H, K = q.shape
+    N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else B
+    dt = {torch.bfloat16: KDA_BF16, torch.float32: KDA_F32}.get(q.dtype, -1)
+    return Desc(B, T, H, K, K, N, dt, KDA_F32, None, 0)
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+        cu_seqlens: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
+        output_final_state: bool = True, out: Optional[torch.Tensor] = None,
+        final_state: Optional[torch.Tensor] = None,
+        stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """KDA chunked forward. Shapes: q, k, v, g [B, T, H, 128]; beta [B, T, H];
+    cu_seqlens int32 [N + 1] (B == 1); initial_state / final state [N, H, 128, 128] fp32.
+
+    Returns (o fp32 [B, T, H, 128], hT or None). Tensors must be contiguous and on
+    one GPU; q, k, v share a dtype (bf16 or fp32); g and beta are fp32.
+    """
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    if g.dtype != torch.float32 or beta.dtype != torch.float32:
+        raise ValueError("g and beta must be float32")
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape or g.shape != q.shape:
+        raise ValueError("q, k, v, g must all be [B, T, H, 128]")
+    if beta.shape != q.shape[:3]:
+        raise ValueError("beta must be [B, T, H]")
+    if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda):
+        raise ValueError("cu_seqlens must be an int32 device tensor")
+    d = _desc(q, cu_seqlens)
+    B, T, H, _ = q.shape
+    if initial_state is not None:
+        if initial_state.dtype != torch.float32 or not initial_state.is_contiguous() \
+                or tuple(initial_state.shape) != (d.num_seqs, H, D, D):
+            raise ValueError("initial_state must be a contiguous float32 [N, H, 128, 128] tensor")
+    o = out if out is not None else torch.empty((B, T, H, D), dtype=torch.float32, device=q.device)
+    hT = None
+    if output_final_state:
+        hT = final_state if final_state is not None else torch.empty(
+            (d.num_seqs, H, D, D), dtype=torch.float32, device=q.device)
+    s = (stream or torch.cuda.current_stream(q.device)).cuda_stream
+    rc = lib().kda_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                       _ptr(initial_state), _ptr(o), _ptr(hT), ctypes.byref(d), ctypes.c_void_p(s))
+    if rc != 0:
+        raise KDAError(rc, "kda_fwd")
+    return o, hT

@@ -1,0 +1,56 @@
+"""ctypes binding of libkda.so: argument marshalling only."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkda.so")
+
+KDA_BF16, KDA_F32 = 0, 1
+STATUS = {0: "KDA_OK", -1: "KDA_ERR_NULL", -2: "KDA_ERR_SHAPE", -3: "KDA_ERR_UNSUPPORTED",
+          -4: "KDA_ERR_DTYPE", -5: "KDA_ERR_WORKSPACE", -6: "KDA_ERR_HIP"}
+
+# every symbol include/kda.h declares
+EXPORTS = ["kda_status_string", "kda_version", "kda_fwd_check", "kda_fwd", "kda_fwd_workspace_size"]
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("V", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
+                ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class KDAError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {STATUS.get(code, code)} ({status_string(code)})")
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"HIP library {LIB_PATH} is not built; run __graft_entry__.build() "
+                              "(or python gated_delta_rule_63_amd/build.py)")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        L.kda_status_string.argtypes = [ctypes.c_int]
+        L.kda_status_string.restype = ctypes.c_char_p
+        L.kda_version.restype = ctypes.c_int32
+        L.kda_fwd_check.argtypes = [P] * 9 + [ctypes.POINTER(Desc)]
+        L.kda_fwd_check.restype = ctypes.c_int
+        L.kda_fwd.argtypes = [P] * 9 + [ctypes.POINTER(Desc), P]
+        L.kda_fwd.restype = ctypes.c_int
+        L.kda_fwd_workspace_size.argtypes = [ctypes.POINTER(Desc)]
+        L.kda_fwd_workspace_size.restype = ctypes.c_size_t
+        _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().kda_status_string(int(code)).decode()

@@ -1,0 +1,27 @@
+// kda_launch.h -- host-side launch interface between the C ABI and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+// Arguments of the fused forward kernel. Layouts are those of include/kda.h.
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    const int32_t* cu;   // device cu_seqlens or nullptr
+    const float* h0;     // nullptr: zero initial state
+    float* o;
+    float* hT;           // nullptr: final state not written
+    int B, T, H, N;
+    int nchains;         // N * H
+};
+
+int fused_workgroups(int nchains);
+hipError_t launch_fwd_fused(const FwdArgs& a, bool f32_inputs, hipStream_t stream);
+
+}  // namespace kda

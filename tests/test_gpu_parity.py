@@ -1,0 +1,106 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Bars: max|err| <= 2e-2 RMS(o) and <= 1e-2 RMS(hT) for bf16 inputs, 1e-4 for
+fp32 inputs; RMS is taken over the whole oracle tensor.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import workloads as W
+from gpu_util import TOL, check, log, rel_err, run_gpu, run_oracle, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_delta_rule_63_amd  # noqa: F401  (fails loudly if the library is missing)
+
+
+# ---------------------------------------------------------------- small configs spanning tiles
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_c0_fp32(seed):
+    check(W.make_inputs(W.CONFIGS["c0"], seed), what=f"c0 seed {seed}")
+
+
+SMALL = [
+    W.variant("c2", T=1000, H=4, name="fixed T=1000 (ragged)"),
+    W.variant("c2", B=2, T=333, H=3, name="batch 2 T=333"),
+    W.variant("c2", T=1000, H=4, h0=True, name="T=1000 with h0"),
+    W.variant("c2", T=777, H=3, h0=True, gate="mild", name="mild decay with h0"),
+    W.variant("c2", T=512, H=2, gate="zero", name="g = 0 (plain delta rule)"),
+    W.variant("c2", T=300, H=2, h0=True, gate="mild", beta="zero", name="beta = 0 (pure decay)"),
+    W.variant("c2", T=300, H=2, keys="onehot", h0=True, gate="mild", name="one-hot keys"),
+    W.variant("c2", T=200, H=2, keys="same", name="identical keys"),
+    W.variant("c2", T=1 + 31 + 32 + 33 + 0 + 100 + 5, H=3, seq_lens=(1, 31, 32, 33, 0, 100, 5), h0=True,
+              name="varlen edge lengths"),
+    W.variant("c2", T=1, H=2, h0=True, name="single token"),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_small(cfg, dtype):
+    check(W.make_inputs(cfg, 7, dtype=dtype), dtype=dtype, what=cfg.name)
+
+
+def test_empty_sequences_keep_state():
+    import torch
+    import gated_delta_rule_63_amd as kda
+    cfg = W.variant("c2", T=40, H=2, seq_lens=(0, 40, 0), h0=True, name="zero-length")
+    inp = W.make_inputs(cfg, 3)
+    o, hT = run_gpu(inp)
+    ro, rs = run_oracle(inp)
+    np.testing.assert_array_equal(hT[0], inp.h0[0])
+    np.testing.assert_array_equal(hT[2], inp.h0[2])
+    assert rel_err(o, ro) <= 2e-2 and rel_err(hT, rs) <= 1e-2
+    # T = 0: nothing to compute, hT = h0
+    t = to_device(W.make_inputs(W.variant("c2", T=8, H=2, h0=True), 0), "bf16")
+    z = {k: (v[:, :0].contiguous() if k in ("q", "k", "v", "g", "beta") else v) for k, v in t.items()}
+    o0, h = kda.fwd(z["q"], z["k"], z["v"], z["g"], z["beta"], initial_state=z["h0"])
+    torch.cuda.synchronize()
+    assert o0.numel() == 0 and torch.equal(h, z["h0"])
+
+
+def test_worked_example_embedded():
+    """The hand-worked 2 x 2 example (tests/golden) embedded in 128 channels, fp32 path."""
+    import torch
+    import gated_delta_rule_63_amd as kda
+    rec = {}
+    for line in open(os.path.join(os.path.dirname(__file__), "golden", "worked_example_2x2.txt")):
+        line = line.split("#")[0].split()
+        if line:
+            rec[line[0]] = np.array([float(x) for x in line[1:]])
+    T = 3
+    z = lambda: np.zeros((1, T, 1, 128), np.float32)
+    q, k, v, g = z(), z(), z(), z()
+    q[0, :, 0, :2] = rec["q"].reshape(T, 2)
+    k[0, :, 0, :2] = rec["k"].reshape(T, 2)
+    v[0, :, 0, :2] = rec["v"].reshape(T, 2)
+    g[0, :, 0, :2] = np.log(rec["alpha"]).reshape(T, 2)
+    beta = rec["beta"].reshape(1, T, 1).astype(np.float32)
+    c = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float32)).cuda()
+    o, hT = kda.fwd(c(q), c(k), c(v), c(g), c(beta))
+    o, hT = o.cpu().numpy(), hT.cpu().numpy()
+    np.testing.assert_allclose(o[0, :, 0, :2], rec["o"].reshape(T, 2), rtol=1e-4, atol=1e-5)
+    np.testing.assert_allclose(hT[0, 0, :2, :2], rec["hT"].reshape(2, 2), rtol=1e-4, atol=1e-5)
+    assert np.all(o[0, :, 0, 2:] == 0) and np.count_nonzero(hT[0, 0]) <= 4
+
+
+# ---------------------------------------------------------------- full-size workloads
+@pytest.mark.parametrize("name", ["c1", "c2", "c3a", "c3b"])
+def test_full_config(name):
+    log(f"[full] {name}: generating inputs")
+    check(W.make_inputs(W.CONFIGS[name], 0), what=f"{name} full")
+
+
+def test_c4_sampled_heads():
+    """T = 131072, H = 32: every output is computed, four heads are compared with the oracle."""
+    log("[full] c4: generating inputs")
+    inp = W.make_inputs(W.CONFIGS["c4"], 0)
+    check(inp, heads=[0, 9, 22, 31], what="c4 heads 0,9,22,31")
