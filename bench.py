@@ -1,0 +1,172 @@
+#!/usr/bin/env python3
+"""KDA chunked prefill throughput on one MI355X.
+
+A step is one kda_fwd call over the whole workload (every token of every head,
+final state included) with the inputs already resident in HBM. Default
+workload: B=1, T=8192, H=96, K=V=128, bf16 q/k/v, fp32 g/beta/state, h0 = 0,
+returns hT (the shape the H20 benchmark table on the toolarium.ru FlashKDA page
+quotes first, section "Что показывают H20-бенчмарки"). Seeded synthetic inputs.
+
+Prints one JSON line with tokens/s, the HBM roofline of the fused kernel
+(algorithmic bytes / measured launch time) and the CPU oracle's throughput on
+this host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+BYTES_PER_TOKEN_HEAD = 3 * 256 + 512 + 4 + 512   # q, k, v bf16 + g fp32 + beta + o fp32
+STATE_BYTES = 128 * 128 * 4                        # one (sequence, head) state, fp32
+FLOPS_PER_TOKEN_HEAD = 141013                      # chunked form at C = 64, see the design doc
+
+
+def alg_bytes(cfg) -> int:
+    per_state = STATE_BYTES * cfg.N * cfg.H
+    return cfg.token_heads * BYTES_PER_TOKEN_HEAD + per_state * (1 + (1 if cfg.h0 else 0))
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_delta_rule_63_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"kda_fwd_fused_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_hash = re.search(r"kernel_source_hash:\s*(\w+)", txt)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_hash or not m_b or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_b.group(1))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--config", default="c2")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--protocol-repeats", type=int, default=5,
+                    help="extra repeats of --steps iterations (the pages' 30/200/5 protocol)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import workloads as W
+    import gated_delta_rule_63_amd as kda
+
+    cfg = W.CONFIGS[args.config]
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+    log(f"[bench] generating {cfg.name} inputs (seed {args.seed})")
+    inp = W.make_inputs(cfg, args.seed)
+    dev = torch.device("cuda:0")
+    if cfg.dtype == "bf16":
+        cvt = lambda x: torch.from_numpy(W.bf16_bits(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        cvt = lambda x: torch.from_numpy(x).to(dev)
+    q, k, v = cvt(inp.q), cvt(inp.k), cvt(inp.v)
+    g, beta = torch.from_numpy(inp.g).to(dev), torch.from_numpy(inp.beta).to(dev)
+    cu = torch.from_numpy(inp.cu_seqlens).to(dev) if inp.cu_seqlens is not None else None
+    h0 = torch.from_numpy(inp.h0).to(dev) if inp.h0 is not None else None
+    o = torch.empty((cfg.B, cfg.T, cfg.H, 128), dtype=torch.float32, device=dev)
+    hT = torch.empty((cfg.N, cfg.H, 128, 128), dtype=torch.float32, device=dev)
+
+    def step():
+        kda.fwd(q, k, v, g, beta, cu_seqlens=cu, initial_state=h0, out=o, final_state=hT)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # the pages' protocol: repeats of `steps` iterations, median of per-iteration means
+    reps = []
+    for _ in range(args.protocol_repeats):
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record(stream)
+        for _ in range(args.steps):
+            step()
+        b_.record(stream)
+        torch.cuda.synchronize()
+        reps.append(a_.elapsed_time(b_) / args.steps)
+
+    tokens = cfg.B * cfg.T
+    value = tokens / (ms / 1e3)
+    bytes_ = alg_bytes(cfg)
+    achieved = bytes_ / (ms / 1e3) / 1e9
+    flops = cfg.token_heads * FLOPS_PER_TOKEN_HEAD
+    traffic = traffic_from_profile(cfg.name)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        log("[bench] CPU oracle baseline (fp64 recurrence, whole workload once)")
+        t0 = time.perf_counter()
+        oracle.kda_ref_fwd(inp.q, inp.k, inp.v, inp.g, inp.beta, cu_seqlens=inp.cu_seqlens, h0=inp.h0)
+        dt = time.perf_counter() - t0
+        cpu = {"value": tokens / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+               "sample": f"the whole {cfg.name} workload once ({cfg.token_heads} token-heads), {dt:.1f} s"}
+
+    desc = f"{cfg.name}: B={cfg.B} T={cfg.T} H={cfg.H} K=V=128 {cfg.dtype} q/k/v, fp32 g/beta/state"
+    if cfg.seq_lens:
+        desc += f", varlen {list(cfg.seq_lens)}"
+    desc += ", h0 given" if cfg.h0 else ", h0 = 0"
+    out = {
+        "metric": "KDA prefill tokens/s (T=8192,H=96,D=128 bf16) + % of MFMA/HBM roofline",
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": desc, "global_batch": cfg.B, "seq_len": cfg.T, "heads": cfg.H,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "kda_fwd_fused", "alg_bytes_per_launch": bytes_},
+        "mfma": {"achieved": flops / (ms / 1e3) / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": flops / (ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+        "protocol": {"repeats": len(reps), "iters": args.steps, "median_ms": float(np.median(reps)) if reps else None,
+                     "min_ms": min(reps) if reps else None, "max_ms": max(reps) if reps else None},
+        "wall_s_timed_region": wall,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
