@@ -23,6 +23,8 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int D = 128;   // K = V = 128
 
@@ -75,6 +77,27 @@ __device__ __forceinline__ void splitbf(float x, __bf16& hi, __bf16& lo) {
     const __bf16 h = cvtbf_once(x);
     hi = h;
     lo = (__bf16)(x - (float)h);
+}
+
+// Pairs: two values rounded together and returned as one packed 32-bit word,
+// the low half holding the first value.
+__device__ __forceinline__ uint32_t pack_f16(float x0, float x1) {
+    f16x2 h = {(_Float16)x0, (_Float16)x1};
+    return __builtin_bit_cast(uint32_t, h);
+}
+__device__ __forceinline__ void split_f16x2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+    f16x2 h = {(_Float16)x0, (_Float16)x1};
+    __asm__ volatile("" : "+v"(h));
+    f16x2 l = {(_Float16)(x0 - (float)h[0]), (_Float16)(x1 - (float)h[1])};
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, l);
+}
+__device__ __forceinline__ void split_bf16x2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+    bf16x2 h = {(__bf16)x0, (__bf16)x1};
+    __asm__ volatile("" : "+v"(h));
+    bf16x2 l = {(__bf16)(x0 - (float)h[0]), (__bf16)(x1 - (float)h[1])};
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, l);
 }
 
 // Load one element of q/k/v as float.

@@ -1,15 +1,15 @@
 // kda_fused.hip -- the fused chunked KDA forward for gfx950.
 //
 // One workgroup owns one (sequence, head, V-block) chain and walks its chunks
-// in order. Per chunk of C = 32 tokens it
-//   (1) scans the log-gate within each 16-token sub-block and forms the gated
-//       key/query factors (per-chunk cumulative log-gate scan);
+// in order. Per chunk of C = 32 tokens (two 16-token sub-blocks) it
+//   (1) scans the log-gate within each sub-block and forms the gated key/query
+//       factors (per-chunk cumulative log-gate scan);
 //   (2) builds the beta-weighted strictly-lower gated K K^T (A) and the lower
-//       gated Q K^T (M) on MFMA, and solves T = (I + A)^{-1}: forward
-//       substitution for the two 16 x 16 diagonal blocks on the A tile staged
-//       in LDS, then T10 = -T11 A10 T00 on fp32 MFMA;
+//       gated Q K^T (M) on MFMA, and inverts the two 16 x 16 diagonal blocks
+//       of I + A by forward substitution on tiles staged in LDS;
 //   (3) advances the 128 x 16-per-wave fp32 state on MFMA:
-//           E = V - (K*gamma) S,  Delta = T Diag(beta) E,
+//           E = V - (K*gamma) S,   Delta = (I + A)^{-1} Diag(beta) E   (block
+//           forward substitution: Delta0 = T00 bE0, Delta1 = T11 (bE1 - A10 Delta0)),
 //           S <- Diag(gamma_last) S + (K*exp(Gamma_last - Gamma))^T Delta;
 //   (4) writes O = (Q*gamma) S + M Delta before the update.
 // These are the four steps of the chunked prefill; the pages credit a chunked
@@ -21,13 +21,14 @@
 //
 // Gating factors are referenced to the middle of each 16-token sub-block, so
 // for g >= -5 every factor lies in [e^-40, e^40] and stays a normal fp32/bf16
-// number (the pages' reason for short chunks: the bf16 numeric range).
+// number (the pages' reason for short chunks: the bf16 numeric range). The
+// scan runs in log2 units so every exponential is one v_exp_f32.
 //
 // Precision. bf16 inputs: the gated K K^T / Q K^T blocks use two-term bf16
 // splits (3 MFMAs per product, fp32 range); (K*gamma) S and (Q*gamma) S use
-// fp16 operands; T Diag(beta) E, M Delta and Kt^T Delta split their V-scale
-// operands into fp16 hi + lo. fp32 inputs: A and M on fp32 MFMA and every
-// other product split into fp16 hi + lo on both sides.
+// fp16 operands; the V-scale operands of the Delta solve, of M Delta and of
+// Kt^T Delta are split into fp16 hi + lo. fp32 inputs: A and M on fp32 MFMA
+// and every other product split into fp16 hi + lo on both sides.
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -42,35 +43,38 @@ constexpr int P = D / VB;      // workgroups per (sequence, head)
 constexpr int LDP = D + 8;     // padded row of a 2-byte [row][128] array
 constexpr int LDF = D + 4;     // padded row of a 4-byte [row][128] array
 constexpr int TP = C + 8;      // padded row of a 2-byte [row][32] array
-constexpr int LDA = C + 4;     // padded row of the fp32 A tile
+constexpr int LDA = 16 + 4;    // padded row of an fp32 16 x 16 tile
 constexpr int LDV = VB + 4;    // padded row of the staged V tile
+constexpr float LOG2E = 1.4426950408889634f;
 static_assert(NT == 4 * (D / 2), "the scan maps one thread to each (channel pair, 8-token quarter)");
 static_assert(C == 32, "the sub-block bookkeeping below is written for two 16-token sub-blocks");
 static_assert(NT * 8 == C * VB, "one 8-element slice of the V tile per thread");
 
+// A/M operands: fp32 for the fp32-MFMA path, [hi, lo] bf16 otherwise.
+template <bool F32> struct AMStore;
+template <> struct AMStore<true> {
+    float Ka[C][LDF], Qa[C][LDF], Kb[C][LDF], Kr[16][LDF];
+};
+template <> struct AMStore<false> {
+    __bf16 Ka[2][C][LDP], Qa[2][C][LDP], Kb[2][C][LDP], Kr[2][16][LDP];
+};
+
 template <bool F32> struct alignas(16) Smem {
-    float Ka[C][LDF];                   // k * exp(Gamma_r - Gamma_mid(block))    row factors
-    float Qa[C][LDF];                   // q * exp(Gamma_r - Gamma_mid(block))
-    float Kb[C][LDF];                   // k * exp(Gamma_mid(block) - Gamma_r)    column factors
-    float Kr[16][LDF];                  // block-0 keys referenced to block 1's middle
+    AMStore<F32> am;                    // Ka, Qa: row factors  k, q * exp(Gamma_r - Gamma_mid)
+                                        // Kb: column factors   k * exp(Gamma_mid - Gamma_r)
+                                        // Kr: block-0 keys referenced to block 1's middle
     _Float16 Kg[F32 ? 2 : 1][C][LDP];   // K * exp(Gamma), channels permuted in 32-groups
     _Float16 Qg[F32 ? 2 : 1][C][LDP];   // Q * exp(Gamma), same order
     _Float16 KtT[2][D][TP];             // (K * exp(Gamma_last - Gamma))^T, [hi, lo][channel][kperm(token)]
-    float A[C][LDA];                    // beta-weighted strictly-lower gated K K^T
-    float Tf[2][16][17];                // fp32 inverses of the two diagonal blocks of I + A
-    _Float16 Tm[2][C][TP];              // (I + A)^{-1}, [hi, lo][row][kperm(col)]
+    float Ad[2][16][LDA];               // diagonal blocks of A for the forward substitution
+    _Float16 A10[2][16][TP];            // A block (rows 16-31, cols 0-15), [hi, lo][row][kperm(col)]
+    _Float16 Tm[2][C][TP];              // block-diagonal (I + A)^{-1}, [hi, lo][row][kperm(col)]
     _Float16 M[2][C][TP];               // lower gated Q K^T, [hi, lo][row][kperm(col)]
     float V[C][LDV];                    // this workgroup's V columns of the chunk
     float gl[D];                        // exp(Gamma_last), the chunk's decay per channel
     float beta[C];
-    float qtot[4][D];                   // sum of g over each 8-token quarter
+    float qtot[4][D];                   // sum of g * log2(e) over each 8-token quarter
 };
-
-template <bool F32>
-__device__ __forceinline__ float ex(float x) {
-    if constexpr (F32) return expf(x);
-    else return __expf(x);
-}
 
 // Registers of one chunk's inputs for thread (channel pair cp, quarter qq).
 template <bool F32> struct Fetch;
@@ -90,21 +94,28 @@ __device__ __forceinline__ float2 bf2(uint32_t u) {
     return make_float2(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
 }
 
+// Per-thread constant offsets (elements) of its loads within a chunk.
+struct Offs {
+    uint32_t gk;   // (8qq) * ts + 2cp : q, k, g of token 8qq, channels 2cp, 2cp+1
+    uint32_t v;    // (tid >> 3) * ts + vcol0 + (tid & 7) * 8 : V tile slice
+};
+
 template <bool F32>
-__device__ __forceinline__ void fetch(Fetch<F32>& f, const FwdArgs& a, long long base, long long ts,
-                                      int row, int h, int cs, int nv, int cp, int qq, int tid, int vcol0) {
+__device__ __forceinline__ void fetch(Fetch<F32>& f, const FwdArgs& a, long long cbase, long long cbeta,
+                                      uint32_t ts, const Offs& of, int nv, int qq, int tid) {
+    const float* gch = a.g + cbase;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
         const int rr = 8 * qq + t;
+        const uint32_t o = of.gk + (uint32_t)t * ts;
         if (rr < nv) {
-            const long long idx = base + (long long)(cs + rr) * ts + 2 * cp;
-            f.g[t] = *reinterpret_cast<const float2*>(a.g + idx);
+            f.g[t] = *reinterpret_cast<const float2*>(gch + o);
             if constexpr (F32) {
-                f.k[t] = *reinterpret_cast<const float2*>(static_cast<const float*>(a.k) + idx);
-                f.q[t] = *reinterpret_cast<const float2*>(static_cast<const float*>(a.q) + idx);
+                f.k[t] = *reinterpret_cast<const float2*>(static_cast<const float*>(a.k) + cbase + o);
+                f.q[t] = *reinterpret_cast<const float2*>(static_cast<const float*>(a.q) + cbase + o);
             } else {
-                f.k[t] = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.k) + idx);
-                f.q[t] = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.q) + idx);
+                f.k[t] = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.k) + cbase + o);
+                f.q[t] = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.q) + cbase + o);
             }
         } else {
             f.g[t] = make_float2(0.f, 0.f);
@@ -112,19 +123,35 @@ __device__ __forceinline__ void fetch(Fetch<F32>& f, const FwdArgs& a, long long
             else { f.k[t] = 0u; f.q[t] = 0u; }
         }
     }
-    f.beta = (tid < nv) ? a.beta[((long long)row * a.T + cs + tid) * a.H + h] : 0.f;
-    const int vr = tid >> 3, vc = (tid & 7) * 8;
-    if (vr < nv) {
-        const long long vi = base + (long long)(cs + vr) * ts + vcol0 + vc;
+    f.beta = (tid < nv) ? a.beta[cbeta + (uint32_t)tid * (uint32_t)a.H] : 0.f;
+    if ((tid >> 3) < nv) {
         if constexpr (F32) {
-            f.v0 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.v) + vi);
-            f.v1 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.v) + vi + 4);
+            const float* vp = static_cast<const float*>(a.v) + cbase + of.v;
+            f.v0 = *reinterpret_cast<const float4*>(vp);
+            f.v1 = *reinterpret_cast<const float4*>(vp + 4);
         } else {
-            f.v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v) + vi);
+            f.v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v) + cbase + of.v);
         }
     } else {
         if constexpr (F32) { f.v0 = make_float4(0.f, 0.f, 0.f, 0.f); f.v1 = f.v0; }
         else f.v = make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
+// Forward substitution of one unit-lower-triangular 16 x 16 block: lane j
+// (of 16) returns column j of (I + Ablk)^{-1}; Ablk rows are read from LDS.
+__device__ __forceinline__ void tri_inverse16(const float (*Ablk)[LDA], int j, float x[16]) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        float s0 = (r == j) ? 1.f : 0.f, s1 = 0.f;
+#pragma unroll
+        for (int i = 0; i + 1 < r; i += 2) {
+            const float2 a2 = *reinterpret_cast<const float2*>(&Ablk[r][i]);
+            s0 -= a2.x * x[i];
+            s1 -= a2.y * x[i + 1];
+        }
+        if (r & 1) s0 -= Ablk[r][r - 1] * x[r - 1];
+        x[r] = s0 + s1;
     }
 }
 
@@ -146,8 +173,9 @@ __global__ __launch_bounds__(NT, 1) void kda_fwd_fused(FwdArgs a) {
     int row, t0, t1;
     if (a.cu) { row = 0; t0 = a.cu[n]; t1 = a.cu[n + 1]; }
     else      { row = n; t0 = 0;       t1 = a.T; }
-    const long long ts = (long long)a.H * D;                       // elements per token
+    const uint32_t ts = (uint32_t)a.H * D;                          // elements per token
     const long long base = (long long)row * a.T * ts + (long long)h * D;
+    const long long bbase = (long long)row * a.T * a.H + h;         // beta of (row, t = 0, h)
     const int vcol0 = vblk * VB;
     const int vc = vcol0 + wave * 16 + l16;                         // this lane's V column
     const long long sbase = ((long long)n * a.H + h) * D * D;
@@ -157,49 +185,66 @@ __global__ __launch_bounds__(NT, 1) void kda_fwd_fused(FwdArgs a) {
     for (int m = 0; m < 8; ++m)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            S[m][j] = a.h0 ? a.h0[sbase + (long long)(16 * m + 4 * grp + j) * D + vc] : 0.f;
+            S[m][j] = a.h0 ? a.h0[sbase + (uint32_t)(16 * m + 4 * grp + j) * D + vc] : 0.f;
 
     const int cp = tid & 63, qq = tid >> 6;      // scan thread: channel pair, 8-token quarter
     const int b = qq >> 1, half = qq & 1;        // its 16-token sub-block and half of it
+    Offs of;
+    of.gk = (uint32_t)(8 * qq) * ts + 2 * cp;
+    of.v = (uint32_t)(tid >> 3) * ts + vcol0 + (tid & 7) * 8;
+    const uint32_t ooff = (uint32_t)(4 * grp) * ts + vc;           // o: this lane's (row 4grp, column vc)
 
-    Fetch<F32> nxt;
-    if (t0 < t1) fetch<F32>(nxt, a, base, ts, row, h, t0, min(C, t1 - t0), cp, qq, tid, vcol0);
+    Fetch<F32> f;
+    if (t0 < t1) fetch<F32>(f, a, base + (long long)t0 * ts, bbase + (long long)t0 * a.H, ts, of, min(C, t1 - t0), qq, tid);
 
     for (int cs = t0; cs < t1; cs += C) {
         const int nv = min(C, t1 - cs);
-        const Fetch<F32> cur = nxt;
-        if (cs + C < t1) fetch<F32>(nxt, a, base, ts, row, h, cs + C, min(C, t1 - cs - C), cp, qq, tid, vcol0);
 
-        // ---- (1) gate scan and gated factors for channels 2cp, 2cp+1, tokens 8qq .. 8qq+7
+        // ---- (1) gate scan (log2 units) over tokens 8qq .. 8qq+7, channels 2cp, 2cp+1
         float L[2][8];
         {
             float r0 = 0.f, r1 = 0.f;
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                r0 += cur.g[t].x;
-                r1 += cur.g[t].y;
+                r0 += f.g[t].x * LOG2E;
+                r1 += f.g[t].y * LOG2E;
                 L[0][t] = r0;
                 L[1][t] = r1;
             }
             *reinterpret_cast<float2*>(&sm.qtot[qq][2 * cp]) = make_float2(r0, r1);
         }
-        if (tid < C) sm.beta[tid] = cur.beta;
+        if (tid < C) sm.beta[tid] = f.beta;
         {
             const int vr = tid >> 3, vcc = (tid & 7) * 8;
-            float vv[8];
+            float4 w0, w1;
             if constexpr (F32) {
-                vv[0] = cur.v0.x; vv[1] = cur.v0.y; vv[2] = cur.v0.z; vv[3] = cur.v0.w;
-                vv[4] = cur.v1.x; vv[5] = cur.v1.y; vv[6] = cur.v1.z; vv[7] = cur.v1.w;
+                w0 = f.v0;
+                w1 = f.v1;
             } else {
-                const float2 p0 = bf2(cur.v.x), p1 = bf2(cur.v.y), p2 = bf2(cur.v.z), p3 = bf2(cur.v.w);
-                vv[0] = p0.x; vv[1] = p0.y; vv[2] = p1.x; vv[3] = p1.y;
-                vv[4] = p2.x; vv[5] = p2.y; vv[6] = p3.x; vv[7] = p3.y;
+                const float2 p0 = bf2(f.v.x), p1 = bf2(f.v.y), p2 = bf2(f.v.z), p3 = bf2(f.v.w);
+                w0 = make_float4(p0.x, p0.y, p1.x, p1.y);
+                w1 = make_float4(p2.x, p2.y, p3.x, p3.y);
             }
-            *reinterpret_cast<float4*>(&sm.V[vr][vcc]) = make_float4(vv[0], vv[1], vv[2], vv[3]);
-            *reinterpret_cast<float4*>(&sm.V[vr][vcc + 4]) = make_float4(vv[4], vv[5], vv[6], vv[7]);
+            *reinterpret_cast<float4*>(&sm.V[vr][vcc]) = w0;
+            *reinterpret_cast<float4*>(&sm.V[vr][vcc + 4]) = w1;
+        }
+        float kv[2][8], qv[2][8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            if constexpr (F32) {
+                kv[0][t] = f.k[t].x; kv[1][t] = f.k[t].y; qv[0][t] = f.q[t].x; qv[1][t] = f.q[t].y;
+            } else {
+                const float2 kk2 = bf2(f.k[t]), qq2 = bf2(f.q[t]);
+                kv[0][t] = kk2.x; kv[1][t] = kk2.y; qv[0][t] = qq2.x; qv[1][t] = qq2.y;
+            }
         }
         __syncthreads();
+        // the registers are consumed: fetch the next chunk while this one computes
+        if (cs + C < t1)
+            fetch<F32>(f, a, base + (long long)(cs + C) * ts, bbase + (long long)(cs + C) * a.H, ts, of,
+                       min(C, t1 - cs - C), qq, tid);
         {
+            float d[2][8], c1[2], c2[2], c3[2];
 #pragma unroll
             for (int ch = 0; ch < 2; ++ch) {
                 const int c = 2 * cp + ch;
@@ -210,51 +255,90 @@ __global__ __launch_bounds__(NT, 1) void kda_fwd_fused(FwdArgs a) {
                 const float off = half ? L7 : 0.f;             // scan offset of this quarter in its sub-block
                 const float start = b ? tot0 : 0.f;            // Gamma at the end of the previous sub-block
                 const float after = b ? 0.f : tot1;            // decay from this sub-block's end to the chunk end
-                const float c1 = ex<F32>(start + L7);          // exp(Gamma_mid)                -> K*gamma, Q*gamma
-                const float c2 = ex<F32>(L15 - L7 + after);    // exp(Gamma_last - Gamma_mid)   -> Kt
-                const float c3 = ex<F32>(L15 - L7 + qt2);      // block 0 -> block 1's middle   -> Kr
-                if (qq == 0) sm.gl[c] = ex<F32>(tot0 + tot1);
+                c1[ch] = exp2f(start + L7);                    // exp(Gamma_mid)               -> K*gamma, Q*gamma
+                c2[ch] = exp2f(L15 - L7 + after);              // exp(Gamma_last - Gamma_mid)  -> Kt
+                c3[ch] = exp2f(L15 - L7 + qt2);                // block 0 -> block 1's middle  -> Kr
+                if (qq == 0) sm.gl[c] = exp2f(tot0 + tot1);
 #pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    const int rr = 8 * qq + t;
-                    const float d = L[ch][t] + off - L7;        // Gamma_r - Gamma_mid, |d| <= 8 * 5
-                    const float e1 = ex<F32>(d), e2 = ex<F32>(-d);
-                    float kv, qv;
-                    if constexpr (F32) { kv = ch ? cur.k[t].y : cur.k[t].x; qv = ch ? cur.q[t].y : cur.q[t].x; }
-                    else { kv = ch ? bf2(cur.k[t]).y : bf2(cur.k[t]).x; qv = ch ? bf2(cur.q[t]).y : bf2(cur.q[t]).x; }
-                    const float ka = kv * e1, qa = qv * e1, kb = kv * e2;
-                    sm.Ka[rr][c] = ka;
-                    sm.Qa[rr][c] = qa;
-                    sm.Kb[rr][c] = kb;
-                    if (b == 0) sm.Kr[rr][c] = kb * c3;
-                    const float kg = ka * c1, qg = qa * c1, kt = kb * c2;
-                    const int cpos = (c & ~31) | kperm(c & 31);
-                    if constexpr (F32) {
-                        split16(kg, sm.Kg[0][rr][cpos], sm.Kg[1][rr][cpos]);
-                        split16(qg, sm.Qg[0][rr][cpos], sm.Qg[1][rr][cpos]);
-                    } else {
-                        sm.Kg[0][rr][cpos] = (_Float16)kg;
-                        sm.Qg[0][rr][cpos] = (_Float16)qg;
+                for (int t = 0; t < 8; ++t) d[ch][t] = L[ch][t] + off - L7;   // |d| <= 8 * 5 * log2(e)
+            }
+            const int cpos = ((2 * cp) & ~31) | kperm((2 * cp) & 31);     // channel pair position in Kg/Qg
+#pragma unroll
+            for (int t = 0; t < 8; t += 2) {
+                float ka[2][2], qa[2][2], kb[2][2], kt[2][2];     // [token][channel]
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int ch = 0; ch < 2; ++ch) {
+                        const float e1 = exp2f(d[ch][t + u]), e2 = exp2f(-d[ch][t + u]);
+                        ka[u][ch] = kv[ch][t + u] * e1;
+                        qa[u][ch] = qv[ch][t + u] * e1;
+                        kb[u][ch] = kv[ch][t + u] * e2;
+                        kt[u][ch] = kb[u][ch] * c2[ch];
                     }
-                    split16(kt, sm.KtT[0][c][kperm(rr)], sm.KtT[1][c][kperm(rr)]);
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int rr = 8 * qq + t + u;
+                    if constexpr (F32) {
+                        *reinterpret_cast<float2*>(&sm.am.Ka[rr][2 * cp]) = make_float2(ka[u][0], ka[u][1]);
+                        *reinterpret_cast<float2*>(&sm.am.Qa[rr][2 * cp]) = make_float2(qa[u][0], qa[u][1]);
+                        *reinterpret_cast<float2*>(&sm.am.Kb[rr][2 * cp]) = make_float2(kb[u][0], kb[u][1]);
+                        if (b == 0)
+                            *reinterpret_cast<float2*>(&sm.am.Kr[rr][2 * cp]) =
+                                make_float2(kb[u][0] * c3[0], kb[u][1] * c3[1]);
+                        uint32_t hi, lo;
+                        split_f16x2(ka[u][0] * c1[0], ka[u][1] * c1[1], hi, lo);
+                        *reinterpret_cast<uint32_t*>(&sm.Kg[0][rr][cpos]) = hi;
+                        *reinterpret_cast<uint32_t*>(&sm.Kg[1][rr][cpos]) = lo;
+                        split_f16x2(qa[u][0] * c1[0], qa[u][1] * c1[1], hi, lo);
+                        *reinterpret_cast<uint32_t*>(&sm.Qg[0][rr][cpos]) = hi;
+                        *reinterpret_cast<uint32_t*>(&sm.Qg[1][rr][cpos]) = lo;
+                    } else {
+                        uint32_t hi, lo;
+                        split_bf16x2(ka[u][0], ka[u][1], hi, lo);
+                        *reinterpret_cast<uint32_t*>(&sm.am.Ka[0][rr][2 * cp]) = hi;
+                        *reinterpret_cast<uint32_t*>(&sm.am.Ka[1][rr][2 * cp]) = lo;
+                        split_bf16x2(qa[u][0], qa[u][1], hi, lo);
+                        *reinterpret_cast<uint32_t*>(&sm.am.Qa[0][rr][2 * cp]) = hi;
+                        *reinterpret_cast<uint32_t*>(&sm.am.Qa[1][rr][2 * cp]) = lo;
+                        split_bf16x2(kb[u][0], kb[u][1], hi, lo);
+                        *reinterpret_cast<uint32_t*>(&sm.am.Kb[0][rr][2 * cp]) = hi;
+                        *reinterpret_cast<uint32_t*>(&sm.am.Kb[1][rr][2 * cp]) = lo;
+                        if (b == 0) {
+                            split_bf16x2(kb[u][0] * c3[0], kb[u][1] * c3[1], hi, lo);
+                            *reinterpret_cast<uint32_t*>(&sm.am.Kr[0][rr][2 * cp]) = hi;
+                            *reinterpret_cast<uint32_t*>(&sm.am.Kr[1][rr][2 * cp]) = lo;
+                        }
+                        *reinterpret_cast<uint32_t*>(&sm.Kg[0][rr][cpos]) = pack_f16(ka[u][0] * c1[0], ka[u][1] * c1[1]);
+                        *reinterpret_cast<uint32_t*>(&sm.Qg[0][rr][cpos]) = pack_f16(qa[u][0] * c1[0], qa[u][1] * c1[1]);
+                    }
+                }
+                // Kt^T: tokens rr, rr+1 sit next to each other in kperm order
+                const int tp = kperm(8 * qq + t);
+#pragma unroll
+                for (int ch = 0; ch < 2; ++ch) {
+                    uint32_t hi, lo;
+                    split_f16x2(kt[0][ch], kt[1][ch], hi, lo);
+                    *reinterpret_cast<uint32_t*>(&sm.KtT[0][2 * cp + ch][tp]) = hi;
+                    *reinterpret_cast<uint32_t*>(&sm.KtT[1][2 * cp + ch][tp]) = lo;
                 }
             }
         }
         __syncthreads();
 
-        // ---- (2a) A and M on 16 x 16 blocks: (0,0), (1,1) diagonal, (1,0) below
+        // ---- (2) A and M blocks; each diagonal block of A is inverted by the wave that built it.
+        // wave 0: A00 -> T00   wave 1: A11 -> T11   wave 2: A10, M10   wave 3: M00, M11
         {
-            // wave 0: A00, A10   wave 1: A11   wave 2: M00, M10   wave 3: M11
-            const bool isM = wave >= 2;
-            const int ntile = (wave & 1) ? 1 : 2;
+            const int ntile = (wave >= 2) ? 2 : 1;
             for (int ti = 0; ti < ntile; ++ti) {
-                const int rb = (wave & 1) ? 1 : ti;       // row block
-                const int cb = (wave & 1) ? 1 : 0;        // column block
+                const bool isM = (wave == 3) || (wave == 2 && ti == 1);
+                const int rb = (wave == 0) ? 0 : (wave == 3 ? ti : 1);
+                const int cb = (wave == 2) ? 0 : rb;
                 const bool diag = (rb == cb);
-                const float* ro = isM ? &sm.Qa[16 * rb + l16][0] : &sm.Ka[16 * rb + l16][0];
-                const float* co = diag ? &sm.Kb[16 * cb + l16][0] : &sm.Kr[l16][0];
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
                 if constexpr (F32) {
+                    const float* ro = isM ? &sm.am.Qa[16 * rb + l16][0] : &sm.am.Ka[16 * rb + l16][0];
+                    const float* co = diag ? &sm.am.Kb[16 * cb + l16][0] : &sm.am.Kr[l16][0];
 #pragma unroll 8
                     for (int kk = 0; kk < D / 4; ++kk)
                         acc = mfma16x4(ro[4 * kk + grp], co[4 * kk + grp], acc);
@@ -262,88 +346,56 @@ __global__ __launch_bounds__(NT, 1) void kda_fwd_fused(FwdArgs a) {
 #pragma unroll
                     for (int kk = 0; kk < D / 32; ++kk) {
                         const int off = 32 * kk + 8 * grp;
-                        const float4 r0 = lds_vec<float4>(ro + off), r1 = lds_vec<float4>(ro + off + 4);
-                        const float4 c0 = lds_vec<float4>(co + off), c1 = lds_vec<float4>(co + off + 4);
-                        const float rv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-                        const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-                        bf16x8 rh, rl, ch, cl;
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            const __bf16 a_hi = cvtbf_once(rv[j]);
-                            rh[j] = a_hi;
-                            rl[j] = (__bf16)(rv[j] - (float)a_hi);
-                            const __bf16 b_hi = cvtbf_once(cv[j]);
-                            ch[j] = b_hi;
-                            cl[j] = (__bf16)(cv[j] - (float)b_hi);
-                        }
+                        const int rrow = 16 * rb + l16;
+                        const bf16x8 rh = lds_vec<bf16x8>(isM ? &sm.am.Qa[0][rrow][off] : &sm.am.Ka[0][rrow][off]);
+                        const bf16x8 rl = lds_vec<bf16x8>(isM ? &sm.am.Qa[1][rrow][off] : &sm.am.Ka[1][rrow][off]);
+                        const bf16x8 ch = lds_vec<bf16x8>(diag ? &sm.am.Kb[0][16 * cb + l16][off] : &sm.am.Kr[0][l16][off]);
+                        const bf16x8 cl = lds_vec<bf16x8>(diag ? &sm.am.Kb[1][16 * cb + l16][off] : &sm.am.Kr[1][l16][off]);
                         acc = mfma16(rh, ch, acc);
                         acc = mfma16(rh, cl, acc);
                         acc = mfma16(rl, ch, acc);
                     }
                 }
+                if (isM) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = 16 * rb + 4 * grp + j, i = 16 * cb + l16;
-                    if (!isM) {
-                        sm.A[r][i] = (i < r) ? sm.beta[r] * acc[j] : 0.f;
-                    } else {
+                    for (int j = 0; j < 4; ++j) {
+                        const int r = 16 * rb + 4 * grp + j, i = 16 * cb + l16;
                         const float val = (i <= r) ? acc[j] : 0.f;
                         split16(val, sm.M[0][r][kperm(i)], sm.M[1][r][kperm(i)]);
+                        if (rb == 0) {   // zero upper-right block of M
+                            sm.M[0][r][kperm(16 + l16)] = (_Float16)0.f;
+                            sm.M[1][r][kperm(16 + l16)] = (_Float16)0.f;
+                        }
+                    }
+                } else if (!diag) {      // A10 as an fp16 [hi, lo] operand over the block-0 token slots
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int r = 4 * grp + j;
+                        split16(sm.beta[16 + r] * acc[j], sm.A10[0][r][kperm(l16)], sm.A10[1][r][kperm(l16)]);
+                        sm.A10[0][r][kperm(16 + l16)] = (_Float16)0.f;
+                        sm.A10[1][r][kperm(16 + l16)] = (_Float16)0.f;
+                    }
+                } else {                 // diagonal block: stage, then invert in this wave
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int r = 4 * grp + j;
+                        sm.Ad[rb][r][l16] = (l16 < r) ? sm.beta[16 * rb + r] * acc[j] : 0.f;
+                    }
+                    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                    float x[16];
+                    tri_inverse16(sm.Ad[rb], l16, x);
+                    if (grp == 0) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            split16(x[r], sm.Tm[0][16 * rb + r][kperm(16 * rb + l16)],
+                                    sm.Tm[1][16 * rb + r][kperm(16 * rb + l16)]);
+                            sm.Tm[0][16 * rb + r][kperm(16 * (1 - rb) + l16)] = (_Float16)0.f;
+                            sm.Tm[1][16 * rb + r][kperm(16 * (1 - rb) + l16)] = (_Float16)0.f;
+                        }
                     }
                 }
             }
-            // the zero upper-right blocks of M and of T
-            if (wave == 3) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    sm.M[0][4 * grp + j][kperm(16 + l16)] = (_Float16)0.f;
-                    sm.M[1][4 * grp + j][kperm(16 + l16)] = (_Float16)0.f;
-                    sm.Tm[0][4 * grp + j][kperm(16 + l16)] = (_Float16)0.f;
-                    sm.Tm[1][4 * grp + j][kperm(16 + l16)] = (_Float16)0.f;
-                }
-            }
-        }
-        __syncthreads();
-
-        // ---- (2b) T = (I + A)^{-1}
-        if (wave == 0) {
-            // diagonal blocks: lane (block bb, column j) forward-substitutes column j
-            const int bb = (lane >> 4) & 1, j = l16;
-            float x[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float* arow = &sm.A[16 * bb + r][16 * bb];
-                float s0 = (r == j) ? 1.f : 0.f, s1 = 0.f;
-#pragma unroll
-                for (int i = 0; i < r; i += 2) {
-                    s0 -= arow[i] * x[i];
-                    if (i + 1 < r) s1 -= arow[i + 1] * x[i + 1];
-                }
-                x[r] = s0 + s1;
-            }
-            if (lane < 32) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    sm.Tf[bb][r][j] = x[r];
-                    split16(x[r], sm.Tm[0][16 * bb + r][kperm(16 * bb + j)], sm.Tm[1][16 * bb + r][kperm(16 * bb + j)]);
-                }
-            }
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            // T10 = -T11 (A10 T00) on fp32 MFMA. Y = A10 T00 lands in accumulator
-            // layout (rows 4grp + jj); fed back as a B operand with the reduction
-            // index of step jj taken as {4g + jj : g = 0..3}.
-            f32x4 Y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                Y = mfma16x4(sm.A[16 + l16][4 * kk + grp], sm.Tf[0][4 * kk + grp][l16], Y);
-            f32x4 Z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                Z = mfma16x4(sm.Tf[1][l16][4 * grp + jj], Y[jj], Z);
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                split16(-Z[jj], sm.Tm[0][16 + 4 * grp + jj][kperm(l16)], sm.Tm[1][16 + 4 * grp + jj][kperm(l16)]);
         }
         __syncthreads();
 
@@ -387,41 +439,69 @@ __global__ __launch_bounds__(NT, 1) void kda_fwd_fused(FwdArgs a) {
                     }
                 }
             }
-            // beta (V - P) as a split B operand over the chunk's 32 tokens
-            f16x8 BEh, BEl;
+            // beta (V - P) for both token tiles
+            float be[2][4];
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int rr = 16 * t + 4 * grp + j;
-                    const half2s u = split16(sm.beta[rr] * (sm.V[rr][wave * 16 + l16] - Pt[t][j]));
-                    BEh[4 * t + j] = u.hi;
-                    BEl[4 * t + j] = u.lo;
+                    be[t][j] = sm.beta[rr] * (sm.V[rr][wave * 16 + l16] - Pt[t][j]);
                 }
-            // Delta = T beta (V - P)
-            f32x4 Dt[2];
+            // Delta0 = T00 bE0
+            const f16x8 Z8 = {0, 0, 0, 0, 0, 0, 0, 0};
+            f16x8 Bh = Z8, Bl = Z8;
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const f16x8 th = lds_vec<f16x8>(&sm.Tm[0][16 * t + l16][8 * grp]);
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                acc = mfma16(th, BEh, acc);
-                acc = mfma16(th, BEl, acc);
-                if constexpr (F32) {
-                    const f16x8 tl = lds_vec<f16x8>(&sm.Tm[1][16 * t + l16][8 * grp]);
-                    acc = mfma16(tl, BEh, acc);
-                }
-                Dt[t] = acc;
+            for (int j = 0; j < 4; ++j) {
+                const half2s u = split16(be[0][j]);
+                Bh[j] = u.hi;
+                Bl[j] = u.lo;
             }
-            f16x8 DBh, DBl;
+            f32x4 D0 = {0.f, 0.f, 0.f, 0.f};
+            {
+                const f16x8 th = lds_vec<f16x8>(&sm.Tm[0][l16][8 * grp]);
+                D0 = mfma16(th, Bh, D0);
+                D0 = mfma16(th, Bl, D0);
+                if constexpr (F32) D0 = mfma16(lds_vec<f16x8>(&sm.Tm[1][l16][8 * grp]), Bh, D0);
+            }
+            f16x8 DBh = Z8, DBl = Z8;
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int j = 0; j < 4; ++j) {
+                const half2s u = split16(D0[j]);
+                DBh[j] = u.hi;
+                DBl[j] = u.lo;
+            }
+            // Delta1 = T11 (bE1 - A10 Delta0)
+            f32x4 X = {0.f, 0.f, 0.f, 0.f};
+            {
+                const f16x8 ah = lds_vec<f16x8>(&sm.A10[0][l16][8 * grp]);
+                X = mfma16(ah, DBh, X);
+                X = mfma16(ah, DBl, X);
+                if constexpr (F32) X = mfma16(lds_vec<f16x8>(&sm.A10[1][l16][8 * grp]), DBh, X);
+            }
+            Bh = Z8;
+            Bl = Z8;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const half2s u = split16(Dt[t][j]);
-                    DBh[4 * t + j] = u.hi;
-                    DBl[4 * t + j] = u.lo;
-                }
+            for (int j = 0; j < 4; ++j) {
+                const half2s u = split16(be[1][j] - X[j]);
+                Bh[4 + j] = u.hi;
+                Bl[4 + j] = u.lo;
+            }
+            f32x4 D1 = {0.f, 0.f, 0.f, 0.f};
+            {
+                const f16x8 th = lds_vec<f16x8>(&sm.Tm[0][16 + l16][8 * grp]);
+                D1 = mfma16(th, Bh, D1);
+                D1 = mfma16(th, Bl, D1);
+                if constexpr (F32) D1 = mfma16(lds_vec<f16x8>(&sm.Tm[1][16 + l16][8 * grp]), Bh, D1);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const half2s u = split16(D1[j]);
+                DBh[4 + j] = u.hi;
+                DBl[4 + j] = u.lo;
+            }
             // O = (Q*gamma) S + M Delta
+            float* och = a.o + base + (long long)cs * ts;
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const f16x8 mh = lds_vec<f16x8>(&sm.M[0][16 * t + l16][8 * grp]);
@@ -433,14 +513,17 @@ __global__ __launch_bounds__(NT, 1) void kda_fwd_fused(FwdArgs a) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int rr = 16 * t + 4 * grp + j;
-                    if (rr < nv) a.o[base + (long long)(cs + rr) * ts + vc] = acc[j];
+                    if (rr < nv) och[ooff + (uint32_t)(16 * t + j) * ts] = acc[j];
                 }
             }
             // S <- Diag(gamma_last) S + Kt^T Delta
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) S[m][j] *= sm.gl[16 * m + 4 * grp + j];
+                const float4 g4 = lds_vec<float4>(&sm.gl[16 * m + 4 * grp]);
+                S[m][0] *= g4.x;
+                S[m][1] *= g4.y;
+                S[m][2] *= g4.z;
+                S[m][3] *= g4.w;
                 const f16x8 kh = lds_vec<f16x8>(&sm.KtT[0][16 * m + l16][8 * grp]);
                 const f16x8 kl = lds_vec<f16x8>(&sm.KtT[1][16 * m + l16][8 * grp]);
                 S[m] = mfma16(kh, DBh, S[m]);
@@ -456,7 +539,7 @@ __global__ __launch_bounds__(NT, 1) void kda_fwd_fused(FwdArgs a) {
         for (int m = 0; m < 8; ++m)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                a.hT[sbase + (long long)(16 * m + 4 * grp + j) * D + vc] = S[m][j];
+                a.hT[sbase + (uint32_t)(16 * m + 4 * grp + j) * D + vc] = S[m][j];
     }
 }
 
