@@ -78,8 +78,9 @@ kda_status_t kda_fwd(const void* q, const void* k, const void* v, const float* g
     a.N = desc->num_seqs;
     a.nchains = desc->num_seqs * desc->H;
     if (a.nchains == 0) return KDA_OK;
-    const hipError_t e = kda::launch_fwd_fused(a, desc->in_dtype == KDA_F32,
-                                               static_cast<hipStream_t>(stream));
+    const hipError_t e = desc->in_dtype == KDA_F32
+                             ? kda::launch_fwd_serial(a, true, static_cast<hipStream_t>(stream))
+                             : kda::launch_fwd_pipe(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

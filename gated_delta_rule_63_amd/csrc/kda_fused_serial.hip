@@ -1,4 +1,5 @@
-// kda_fused.hip -- the fused chunked KDA forward for gfx950.
+// kda_fused_serial.hip -- the fused chunked KDA forward for gfx950, one phase at a time.
+// It serves fp32 inputs; bf16 inputs take the pipelined kernel (kda_fused_pipe.hip).
 //
 // One workgroup owns one (sequence, head, V-block) chain and walks its chunks
 // in order. Per chunk of C = 32 tokens (two 16-token sub-blocks) it
@@ -545,13 +546,13 @@ __global__ __launch_bounds__(NT, 1) void kda_fwd_fused(FwdArgs a) {
 
 }  // namespace fused
 
-int fused_workgroups(int nchains) {
+int serial_workgroups(int nchains) {
     const int groups = (nchains + 7) / 8;
     return groups * 8 * fused::P;
 }
 
-hipError_t launch_fwd_fused(const FwdArgs& a, bool f32_inputs, hipStream_t stream) {
-    const int grid = fused_workgroups(a.nchains);
+hipError_t launch_fwd_serial(const FwdArgs& a, bool f32_inputs, hipStream_t stream) {
+    const int grid = serial_workgroups(a.nchains);
     if (grid == 0) return hipSuccess;
     if (f32_inputs)
         hipLaunchKernelGGL(fused::kda_fwd_fused<true>, dim3(grid), dim3(fused::NT), 0, stream, a);

@@ -21,7 +21,11 @@ struct FwdArgs {
     int nchains;         // N * H
 };
 
-int fused_workgroups(int nchains);
-hipError_t launch_fwd_fused(const FwdArgs& a, bool f32_inputs, hipStream_t stream);
+// One phase at a time (both input dtypes); used for fp32 inputs.
+int serial_workgroups(int nchains);
+hipError_t launch_fwd_serial(const FwdArgs& a, bool f32_inputs, hipStream_t stream);
+// Helper waves prepare chunk i+1 while state waves advance chunk i (bf16 inputs).
+int pipe_workgroups(int nchains);
+hipError_t launch_fwd_pipe(const FwdArgs& a, hipStream_t stream);
 
 }  // namespace kda
