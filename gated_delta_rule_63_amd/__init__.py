@@ -14,9 +14,9 @@ from typing import Optional, Tuple
 
 import torch
 
-from ._lib import KDA_BF16, KDA_F32, Desc, KDAError, lib, status_string  # noqa: F401
+from ._lib import KDA_BF16, KDA_F32, Desc, KDAError, Layout, lib, status_string  # noqa: F401
 
-__all__ = ["fwd", "KDAError", "status_string", "version"]
+__all__ = ["fwd", "fwd_staged", "Staged", "KDAError", "status_string", "version"]
 
 D = 128
 
@@ -36,17 +36,7 @@ def _desc(q: torch.Tensor, cu_seqlens: Optional[torch.Tensor]) -> Desc:
     return Desc(B, T, H, K, K, N, dt, KDA_F32, None, 0)
 
 
-def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
-        cu_seqlens: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
-        output_final_state: bool = True, out: Optional[torch.Tensor] = None,
-        final_state: Optional[torch.Tensor] = None,
-        stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """KDA chunked forward. Shapes: q, k, v, g [B, T, H, 128]; beta [B, T, H];
-    cu_seqlens int32 [N + 1] (B == 1); initial_state / final state [N, H, 128, 128] fp32.
-
-    Returns (o fp32 [B, T, H, 128], hT or None). Tensors must be contiguous and on
-    one GPU; q, k, v share a dtype (bf16 or fp32); g and beta are fp32.
-    """
+def _check_inputs(q, k, v, g, beta, cu_seqlens):
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous device tensor")
@@ -60,6 +50,20 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
         raise ValueError("beta must be [B, T, H]")
     if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda):
         raise ValueError("cu_seqlens must be an int32 device tensor")
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+        cu_seqlens: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
+        output_final_state: bool = True, out: Optional[torch.Tensor] = None,
+        final_state: Optional[torch.Tensor] = None,
+        stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """KDA chunked forward. Shapes: q, k, v, g [B, T, H, 128]; beta [B, T, H];
+    cu_seqlens int32 [N + 1] (B == 1); initial_state / final state [N, H, 128, 128] fp32.
+
+    Returns (o fp32 [B, T, H, 128], hT or None). Tensors must be contiguous and on
+    one GPU; q, k, v share a dtype (bf16 or fp32); g and beta are fp32.
+    """
+    _check_inputs(q, k, v, g, beta, cu_seqlens)
     d = _desc(q, cu_seqlens)
     B, T, H, _ = q.shape
     if initial_state is not None:
@@ -77,3 +81,87 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
     if rc != 0:
         raise KDAError(rc, "kda_fwd")
     return o, hT
+
+
+class Staged:
+    """The staged path (a0 chunk map, a1 gate scan, a2 intra-chunk, a3 recurrence,
+    a4 output) over one workspace. Each stage is one kernel on the current stream;
+    the intermediates are tensor views into the workspace (fp32, 32-token chunks)."""
+
+    def __init__(self, q, k, v, g, beta, cu_seqlens=None, initial_state=None, workspace=None):
+        _check_inputs(q, k, v, g, beta, cu_seqlens)
+        self.q, self.k, self.v, self.g, self.beta, self.cu = q, k, v, g, beta, cu_seqlens
+        self.h0 = initial_state
+        self.desc = _desc(q, cu_seqlens)
+        L = Layout()
+        rc = lib().kda_staged_layout(ctypes.byref(self.desc), ctypes.byref(L))
+        if rc != 0:
+            raise KDAError(rc, "kda_staged_layout")
+        self.layout = L
+        if workspace is None:
+            workspace = torch.empty(L.total, dtype=torch.uint8, device=q.device)
+        if workspace.numel() < L.total:
+            raise ValueError("workspace too small")
+        self.ws = workspace
+        self.desc.workspace = ctypes.c_void_p(workspace.data_ptr())
+        self.desc.workspace_bytes = workspace.numel()
+        B, T, H, _ = q.shape
+        N, S, C = self.desc.num_seqs, L.nslots, L.chunk
+
+        def view(off, shape, dtype):
+            n = 1
+            for x in shape:
+                n *= x
+            item = torch.empty((), dtype=dtype).element_size()
+            return workspace[off:off + n * item].view(dtype).view(*shape)
+
+        self.map = view(L.map, (S, 4), torch.int32)
+        self.seqinfo = view(L.seqinfo, (max(N, 1), 2), torch.int32)
+        self.Gamma = view(L.Gamma, (B, T, H, D), torch.float32)
+        self.gl = view(L.gl, (S, H, D), torch.float32)
+        self.W = view(L.W, (B, T, H, D), torch.float32)
+        self.U = view(L.U, (B, T, H, D), torch.float32)
+        self.Kt = view(L.Kt, (B, T, H, D), torch.float32)
+        self.Qg = view(L.Qg, (B, T, H, D), torch.float32)
+        self.M = view(L.M, (S, H, C, C), torch.float32)
+        self.hc = view(L.hc, (S, H, D, D), torch.float32)
+        self.Delta = view(L.Delta, (B, T, H, D), torch.float32)
+
+    def _s(self):
+        return ctypes.c_void_p(torch.cuda.current_stream(self.q.device).cuda_stream)
+
+    def _rc(self, rc, name):
+        if rc != 0:
+            raise KDAError(rc, name)
+
+    def chunk_map(self):
+        self._rc(lib().kda_stage_chunk_map(_ptr(self.cu), ctypes.byref(self.desc), self._s()), "kda_stage_chunk_map")
+
+    def gate_scan(self):
+        self._rc(lib().kda_stage_gate_scan(_ptr(self.g), ctypes.byref(self.desc), self._s()), "kda_stage_gate_scan")
+
+    def intra(self):
+        self._rc(lib().kda_stage_intra(_ptr(self.q), _ptr(self.k), _ptr(self.v), _ptr(self.beta),
+                                       ctypes.byref(self.desc), self._s()), "kda_stage_intra")
+
+    def recurrence(self, final_state=None):
+        self._rc(lib().kda_stage_recurrence(_ptr(self.h0), _ptr(final_state), ctypes.byref(self.desc), self._s()),
+                 "kda_stage_recurrence")
+
+    def output(self, o):
+        self._rc(lib().kda_stage_output(_ptr(o), ctypes.byref(self.desc), self._s()), "kda_stage_output")
+
+
+def fwd_staged(q, k, v, g, beta, cu_seqlens=None, initial_state=None, output_final_state=True,
+               workspace=None):
+    """kda_fwd_staged: the five stage kernels in order. Returns (o, hT or None, Staged)."""
+    st = Staged(q, k, v, g, beta, cu_seqlens, initial_state, workspace)
+    B, T, H, _ = q.shape
+    o = torch.empty((B, T, H, D), dtype=torch.float32, device=q.device)
+    hT = torch.empty((st.desc.num_seqs, H, D, D), dtype=torch.float32, device=q.device) \
+        if output_final_state else None
+    rc = lib().kda_fwd_staged(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                              _ptr(initial_state), _ptr(o), _ptr(hT), ctypes.byref(st.desc), st._s())
+    if rc != 0:
+        raise KDAError(rc, "kda_fwd_staged")
+    return o, hT, st

@@ -12,7 +12,9 @@ STATUS = {0: "KDA_OK", -1: "KDA_ERR_NULL", -2: "KDA_ERR_SHAPE", -3: "KDA_ERR_UNS
           -4: "KDA_ERR_DTYPE", -5: "KDA_ERR_WORKSPACE", -6: "KDA_ERR_HIP"}
 
 # every symbol include/kda.h declares
-EXPORTS = ["kda_status_string", "kda_version", "kda_fwd_check", "kda_fwd", "kda_fwd_workspace_size"]
+EXPORTS = ["kda_status_string", "kda_version", "kda_fwd_check", "kda_fwd", "kda_staged_layout",
+           "kda_fwd_workspace_size", "kda_stage_chunk_map", "kda_stage_gate_scan", "kda_stage_intra",
+           "kda_stage_recurrence", "kda_stage_output", "kda_fwd_staged"]
 
 
 class Desc(ctypes.Structure):
@@ -20,6 +22,12 @@ class Desc(ctypes.Structure):
                 ("K", ctypes.c_int32), ("V", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
                 ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("nslots", ctypes.c_int32), ("chunk", ctypes.c_int32)] + [
+        (n, ctypes.c_size_t) for n in ("map", "seqinfo", "Gamma", "gl", "W", "U", "Kt", "Qg", "M", "hc",
+                                       "Delta", "total")]
 
 
 class KDAError(RuntimeError):
@@ -48,6 +56,16 @@ def lib():
         L.kda_fwd.restype = ctypes.c_int
         L.kda_fwd_workspace_size.argtypes = [ctypes.POINTER(Desc)]
         L.kda_fwd_workspace_size.restype = ctypes.c_size_t
+        L.kda_staged_layout.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Layout)]
+        L.kda_staged_layout.restype = ctypes.c_int
+        D = ctypes.POINTER(Desc)
+        for name, n in (("kda_stage_chunk_map", 1), ("kda_stage_gate_scan", 1), ("kda_stage_intra", 4),
+                        ("kda_stage_recurrence", 2), ("kda_stage_output", 1)):
+            fn = getattr(L, name)
+            fn.argtypes = [P] * n + [D, P]
+            fn.restype = ctypes.c_int
+        L.kda_fwd_staged.argtypes = [P] * 9 + [D, P]
+        L.kda_fwd_staged.restype = ctypes.c_int
         _lib = L
     return _lib
 

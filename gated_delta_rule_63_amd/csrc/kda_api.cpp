@@ -4,7 +4,10 @@
 
 #include <limits.h>
 
+#include <algorithm>
+
 #include "kda_launch.h"
+#include "kda_stages.h"
 
 namespace {
 
@@ -29,6 +32,81 @@ kda_status_t check(const void* q, const void* k, const void* v, const float* g, 
     if (tok > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL;
     return KDA_OK;
 }
+
+// Shape-only validation shared by the staged entry points.
+kda_status_t check_desc(const kda_desc_t* d, bool varlen) {
+    if (!d) return KDA_ERR_NULL;
+    if (d->B < 1 || d->T < 0 || d->H < 1 || d->K < 1 || d->V < 1) return KDA_ERR_SHAPE;
+    if (d->K != 128 || d->V != 128) return KDA_ERR_UNSUPPORTED;
+    if (d->in_dtype != KDA_BF16 && d->in_dtype != KDA_F32) return KDA_ERR_DTYPE;
+    if (d->out_dtype != KDA_BF16 && d->out_dtype != KDA_F32) return KDA_ERR_DTYPE;
+    if (d->out_dtype != KDA_F32) return KDA_ERR_UNSUPPORTED;
+    if (varlen ? (d->B != 1 || d->num_seqs < 0) : (d->num_seqs != d->B)) return KDA_ERR_SHAPE;
+    return KDA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Layout of the staged path's workspace. Whether the descriptor is varlen is
+// not part of kda_desc_t, so the slot count covers both cases: the larger of
+// B*ceil(T/32) and ceil(T/32) + N.
+kda_status_t layout(const kda_desc_t* d, kda_staged_layout_t* L) {
+    const kda_status_t st = check_desc(d, d && d->num_seqs != d->B);
+    if (st != KDA_OK) return st;
+    const long long C = kda::kStageChunk;
+    const long long nchunk = (d->T + C - 1) / C;
+    const long long nslots = std::max((long long)d->B * nchunk, nchunk + d->num_seqs);
+    if (nslots > INT_MAX / 4) return KDA_ERR_SHAPE;
+    const size_t tok = (size_t)d->B * d->T * d->H * 128 * sizeof(float);
+    size_t off = 0;
+    auto take = [&](size_t bytes) { const size_t o = off; off = align256(off + bytes); return o; };
+    L->nslots = (int32_t)nslots;
+    L->chunk = (int32_t)C;
+    L->map = take((size_t)nslots * 4 * sizeof(int32_t));
+    L->seqinfo = take((size_t)std::max(d->num_seqs, 1) * 2 * sizeof(int32_t));
+    L->Gamma = take(tok);
+    L->gl = take((size_t)nslots * d->H * 128 * sizeof(float));
+    L->W = take(tok);
+    L->U = take(tok);
+    L->Kt = take(tok);
+    L->Qg = take(tok);
+    L->M = take((size_t)nslots * d->H * C * C * sizeof(float));
+    L->hc = take((size_t)nslots * d->H * 128 * 128 * sizeof(float));
+    L->Delta = take(tok);
+    L->total = off;
+    return KDA_OK;
+}
+
+// StageArgs pointing into the caller's workspace.
+kda_status_t stage_args(const kda_desc_t* d, const int32_t* cu, kda::StageArgs* a) {
+    kda_staged_layout_t L;
+    const kda_status_t st = layout(d, &L);
+    if (st != KDA_OK) return st;
+    if (!d->workspace || d->workspace_bytes < L.total) return KDA_ERR_WORKSPACE;
+    char* w = static_cast<char*>(d->workspace);
+    *a = kda::StageArgs{};
+    a->cu = cu;
+    a->map = reinterpret_cast<int32_t*>(w + L.map);
+    a->seqinfo = reinterpret_cast<int32_t*>(w + L.seqinfo);
+    a->Gamma = reinterpret_cast<float*>(w + L.Gamma);
+    a->gl = reinterpret_cast<float*>(w + L.gl);
+    a->W = reinterpret_cast<float*>(w + L.W);
+    a->U = reinterpret_cast<float*>(w + L.U);
+    a->Kt = reinterpret_cast<float*>(w + L.Kt);
+    a->Qg = reinterpret_cast<float*>(w + L.Qg);
+    a->M = reinterpret_cast<float*>(w + L.M);
+    a->hc = reinterpret_cast<float*>(w + L.hc);
+    a->Delta = reinterpret_cast<float*>(w + L.Delta);
+    a->B = d->B;
+    a->T = d->T;
+    a->H = d->H;
+    a->N = d->num_seqs;
+    a->nslots = L.nslots;
+    a->f32 = d->in_dtype == KDA_F32;
+    return KDA_OK;
+}
+
+kda_status_t hip_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
 
 }  // namespace
 
@@ -84,14 +162,88 @@ kda_status_t kda_fwd(const void* q, const void* k, const void* v, const float* g
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+kda_status_t kda_staged_layout(const kda_desc_t* desc, kda_staged_layout_t* out) {
+    if (!out) return KDA_ERR_NULL;
+    return layout(desc, out);
+}
+
 size_t kda_fwd_workspace_size(const kda_desc_t* desc) {
-    if (check(reinterpret_cast<const void*>(1), reinterpret_cast<const void*>(1),
-              reinterpret_cast<const void*>(1), reinterpret_cast<const float*>(1),
-              reinterpret_cast<const float*>(1), nullptr, reinterpret_cast<const void*>(1),
-              desc) != KDA_OK &&
-        !(desc && desc->B == 1))
-        return 0;
-    return 0;
+    kda_staged_layout_t L;
+    return layout(desc, &L) == KDA_OK ? L.total : 0;
+}
+
+kda_status_t kda_stage_chunk_map(const int32_t* cu_seqlens, const kda_desc_t* desc, void* stream) {
+    if (desc && cu_seqlens == nullptr && desc->num_seqs != desc->B) return KDA_ERR_SHAPE;
+    kda::StageArgs a;
+    const kda_status_t st = stage_args(desc, cu_seqlens, &a);
+    if (st != KDA_OK) return st;
+    if (cu_seqlens && desc->B != 1) return KDA_ERR_SHAPE;
+    return hip_status(kda::launch_chunk_map(a, static_cast<hipStream_t>(stream)));
+}
+
+kda_status_t kda_stage_gate_scan(const float* g, const kda_desc_t* desc, void* stream) {
+    kda::StageArgs a;
+    const kda_status_t st = stage_args(desc, nullptr, &a);
+    if (st != KDA_OK) return st;
+    if (!g && desc->T > 0) return KDA_ERR_NULL;
+    a.g = g;
+    return hip_status(kda::launch_gate_scan(a, static_cast<hipStream_t>(stream)));
+}
+
+kda_status_t kda_stage_intra(const void* q, const void* k, const void* v, const float* beta,
+                             const kda_desc_t* desc, void* stream) {
+    kda::StageArgs a;
+    const kda_status_t st = stage_args(desc, nullptr, &a);
+    if (st != KDA_OK) return st;
+    if ((!q || !k || !v || !beta) && desc->T > 0) return KDA_ERR_NULL;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.beta = beta;
+    return hip_status(kda::launch_intra(a, static_cast<hipStream_t>(stream)));
+}
+
+kda_status_t kda_stage_recurrence(const float* h0, float* hT, const kda_desc_t* desc, void* stream) {
+    kda::StageArgs a;
+    const kda_status_t st = stage_args(desc, nullptr, &a);
+    if (st != KDA_OK) return st;
+    a.h0 = h0;
+    a.hT = hT;
+    return hip_status(kda::launch_recurrence(a, static_cast<hipStream_t>(stream)));
+}
+
+kda_status_t kda_stage_output(void* o, const kda_desc_t* desc, void* stream) {
+    kda::StageArgs a;
+    const kda_status_t st = stage_args(desc, nullptr, &a);
+    if (st != KDA_OK) return st;
+    if (!o && desc->T > 0) return KDA_ERR_NULL;
+    a.o = static_cast<float*>(o);
+    return hip_status(kda::launch_output(a, static_cast<hipStream_t>(stream)));
+}
+
+kda_status_t kda_fwd_staged(const void* q, const void* k, const void* v, const float* g,
+                            const float* beta, const int32_t* cu_seqlens, const float* h0, void* o,
+                            float* hT, const kda_desc_t* desc, void* stream) {
+    kda_status_t st = check(q, k, v, g, beta, cu_seqlens, o, desc);
+    if (st != KDA_OK) return st;
+    kda::StageArgs a;
+    st = stage_args(desc, cu_seqlens, &a);
+    if (st != KDA_OK) return st;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.h0 = h0;
+    a.hT = hT;
+    a.o = static_cast<float*>(o);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = kda::launch_chunk_map(a, s);
+    if (e == hipSuccess) e = kda::launch_gate_scan(a, s);
+    if (e == hipSuccess) e = kda::launch_intra(a, s);
+    if (e == hipSuccess) e = kda::launch_recurrence(a, s);
+    if (e == hipSuccess) e = kda::launch_output(a, s);
+    return hip_status(e);
 }
 
 }  // extern "C"

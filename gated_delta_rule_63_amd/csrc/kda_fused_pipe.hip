@@ -112,18 +112,26 @@ __device__ __forceinline__ void hfetch(HFetch& f, const FwdArgs& a, long long cb
 }
 
 // Forward substitution of one unit-lower-triangular 16 x 16 block: lane j
-// (of 16) returns column j of (I + Ablk)^{-1}.
+// (of 16) returns column j of (I + Ablk)^{-1}. The lower triangle is read into
+// registers first (36 broadcast 16-byte reads), so the 16 dependent row steps
+// wait on FMAs only, not on LDS round trips.
 __device__ __forceinline__ void tri_inverse16(const float (*Ablk)[LDA], int j, float x[16]) {
+    float4 ar[16][4];
+#pragma unroll
+    for (int r = 1; r < 16; ++r)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (4 * q < r) ar[r][q] = *reinterpret_cast<const float4*>(&Ablk[r][4 * q]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         float s0 = (r == j) ? 1.f : 0.f, s1 = 0.f;
 #pragma unroll
-        for (int i = 0; i + 1 < r; i += 2) {
-            const float2 a2 = *reinterpret_cast<const float2*>(&Ablk[r][i]);
-            s0 -= a2.x * x[i];
-            s1 -= a2.y * x[i + 1];
+        for (int i = 0; i < r; ++i) {
+            const float4 v4 = ar[r][i >> 2];
+            const float av = (i & 3) == 0 ? v4.x : (i & 3) == 1 ? v4.y : (i & 3) == 2 ? v4.z : v4.w;
+            if (i & 1) s1 -= av * x[i];
+            else s0 -= av * x[i];
         }
-        if (r & 1) s0 -= Ablk[r][r - 1] * x[r - 1];
         x[r] = s0 + s1;
     }
 }

@@ -74,8 +74,8 @@ typedef struct kda_desc {
     int32_t num_seqs;        /* N: equals B without cu_seqlens; count of sequences with it */
     int32_t in_dtype;        /* kda_dtype_t of q, k, v                                    */
     int32_t out_dtype;       /* kda_dtype_t of o; only KDA_F32 is built                   */
-    void* workspace;         /* device scratch for the staged path (kda_fwd_staged)       */
-    size_t workspace_bytes;  /* its size; kda_fwd itself needs none                       */
+    void* workspace;         /* device scratch of the staged path (kda_fwd_staged, kda_stage_*) */
+    size_t workspace_bytes;  /* its size; kda_fwd itself needs none                             */
 } kda_desc_t;
 
 /* Text for a status code (static storage, never NULL). */
@@ -99,8 +99,58 @@ kda_status_t kda_fwd(const void* q, const void* k, const void* v, const float* g
                      const float* beta, const int32_t* cu_seqlens, const float* h0,
                      void* o, float* hT, const kda_desc_t* desc, void* stream);
 
-/* Bytes of workspace kda_fwd_staged needs for this descriptor (0 on error). */
+/* ---------------------------------------------------------------------------
+ * Staged path. The same chunked forward as four kernels (plus a chunk map)
+ * that keep every intermediate in a caller-owned device workspace
+ * (desc->workspace, desc->workspace_bytes), all in fp32 with 32-token chunks.
+ * It is slower than kda_fwd (it writes and re-reads the intermediates) and
+ * exists so that each step can be run, checked and timed on its own. The
+ * pages describe the method's forward as a chunked two-kernel design
+ * (toolarium.ru page, section "Где ограничения прямо сейчас").
+ *
+ * Workspace contents, at the byte offsets kda_staged_layout reports:
+ *   map      int32 [nslots][4]  (sequence, first token, valid tokens, batch row);
+ *                               unused slots have sequence -1 and 0 tokens
+ *   seqinfo  int32 [N][2]       (first slot, chunk count) per sequence
+ *   Gamma    fp32 [B,T,H,128]   in-chunk cumulative sum of g (a1)
+ *   gl       fp32 [nslots,H,128] exp(Gamma at the chunk's last token) (a1)
+ *   W, U, Kt, Qg  fp32 [B,T,H,128]  (a2): W = (I+A)^{-1} Diag(beta)(K*exp Gamma),
+ *                               U = (I+A)^{-1} Diag(beta) V, Kt = K*exp(Gamma_last-Gamma),
+ *                               Qg = Q*exp(Gamma)
+ *   M        fp32 [nslots,H,32,32]  lower-triangular gated Q K^T (a2)
+ *   hc       fp32 [nslots,H,128,128] state entering each chunk (a3)
+ *   Delta    fp32 [B,T,H,128]   U - W h_c (a3)
+ * A workspace is used by one call sequence at a time.
+ * ------------------------------------------------------------------------- */
+typedef struct kda_staged_layout {
+    int32_t nslots;   /* chunk slots: B*ceil(T/32), or ceil(T/32) + N with cu_seqlens */
+    int32_t chunk;    /* 32 */
+    size_t map, seqinfo, Gamma, gl, W, U, Kt, Qg, M, hc, Delta;   /* byte offsets */
+    size_t total;     /* bytes */
+} kda_staged_layout_t;
+
+/* Fills *out for this descriptor (host only). */
+kda_status_t kda_staged_layout(const kda_desc_t* desc, kda_staged_layout_t* out);
+
+/* Bytes of workspace the staged path needs for this descriptor (0 on error). */
 size_t kda_fwd_workspace_size(const kda_desc_t* desc);
+
+/* a0: chunk map from cu_seqlens (NULL: B rows of T tokens), built on the device. */
+kda_status_t kda_stage_chunk_map(const int32_t* cu_seqlens, const kda_desc_t* desc, void* stream);
+/* a1: per-chunk cumulative log-gate scan (needs a0). */
+kda_status_t kda_stage_gate_scan(const float* g, const kda_desc_t* desc, void* stream);
+/* a2: intra-chunk step: gated K K^T, its unit-lower-triangular inverse, W, U, Kt, Qg, M (needs a1). */
+kda_status_t kda_stage_intra(const void* q, const void* k, const void* v, const float* beta,
+                             const kda_desc_t* desc, void* stream);
+/* a3: inter-chunk recurrence per (sequence, head, 16-column V-block): h_c, Delta, hT (needs a2). */
+kda_status_t kda_stage_recurrence(const float* h0, float* hT, const kda_desc_t* desc, void* stream);
+/* a4: output O = Qg h_c + M Delta (needs a3). */
+kda_status_t kda_stage_output(void* o, const kda_desc_t* desc, void* stream);
+
+/* a0..a4 in order: the same contract as kda_fwd, plus the workspace. */
+kda_status_t kda_fwd_staged(const void* q, const void* k, const void* v, const float* g,
+                            const float* beta, const int32_t* cu_seqlens, const float* h0,
+                            void* o, float* hT, const kda_desc_t* desc, void* stream);
 
 #ifdef __cplusplus
 }

@@ -1,0 +1,91 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/kda.h declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+@pytest.fixture(scope="module")
+def K():
+    import gated_delta_rule_63_amd as kda
+    return kda
+
+
+def declared_functions():
+    txt = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_function(K):
+    names = declared_functions()
+    assert len(names) >= 12, names
+    lib = ctypes.CDLL(K._lib.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/kda.h but not exported"
+    assert sorted(K._lib.EXPORTS) == names
+
+
+def test_version_and_status_strings(K):
+    assert K.version() == 100
+    for code in [0, -1, -2, -3, -4, -5, -6]:
+        assert K.status_string(code)
+    assert "unknown" in K.status_string(-99)
+
+
+def desc(K, B=1, T=64, H=2, Kd=128, V=128, N=None, in_dt=0, out_dt=1):
+    return K.Desc(B, T, H, Kd, V, B if N is None else N, in_dt, out_dt, None, 0)
+
+
+P = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails or succeeds before any launch
+
+
+def check(K, d, cu=None, q=P, o=P):
+    return K.lib().kda_fwd_check(q, P, P, P, P, cu, None, o, None, ctypes.byref(d))
+
+
+def test_validation_codes(K):
+    assert check(K, desc(K)) == 0
+    assert K.lib().kda_fwd_check(P, P, P, P, P, None, None, P, None, None) == -1          # NULL desc
+    assert check(K, desc(K, Kd=64)) == -3 and check(K, desc(K, V=256)) == -3              # K, V != 128
+    assert check(K, desc(K, in_dt=7)) == -4 and check(K, desc(K, out_dt=9)) == -4
+    assert check(K, desc(K, out_dt=0)) == -3                                              # bf16 o not built
+    assert check(K, desc(K, B=0)) == -2 and check(K, desc(K, T=-1)) == -2
+    assert check(K, desc(K, B=2, N=3)) == -2                                              # N != B without cu
+    assert check(K, desc(K, B=2, N=3), cu=P) == -2                                        # varlen needs B == 1
+    assert check(K, desc(K, N=5), cu=P) == 0
+    assert check(K, desc(K), q=None) == -1 and check(K, desc(K), o=None) == -1
+    assert check(K, desc(K, T=0), q=None, o=None) == 0                                    # empty: no data needed
+
+
+def test_fwd_rejects_before_launch(K):
+    """Argument errors return without touching the device (this machine has none)."""
+    d = desc(K, Kd=64)
+    assert K.lib().kda_fwd(P, P, P, P, P, None, None, P, None, ctypes.byref(d), None) == -3
+    d = desc(K)
+    assert K.lib().kda_fwd_staged(P, P, P, P, P, None, None, P, None, ctypes.byref(d), None) == -5   # no workspace
+    for fn, n in (("kda_stage_gate_scan", 1), ("kda_stage_intra", 4), ("kda_stage_recurrence", 2),
+                  ("kda_stage_output", 1)):
+        assert getattr(K.lib(), fn)(*([P] * n), ctypes.byref(d), None) == -5
+    assert K.lib().kda_stage_chunk_map(None, ctypes.byref(d), None) == -5
+    d.workspace, d.workspace_bytes = P, 16
+    assert K.lib().kda_stage_output(P, ctypes.byref(d), None) == -5                       # too small
+
+
+def test_staged_layout(K):
+    L = K.Layout()
+    d = desc(K, B=1, T=8192, H=96)
+    assert K.lib().kda_staged_layout(ctypes.byref(d), ctypes.byref(L)) == 0
+    assert L.chunk == 32 and L.nslots == 257
+    offs = [L.map, L.seqinfo, L.Gamma, L.gl, L.W, L.U, L.Kt, L.Qg, L.M, L.hc, L.Delta]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    tok = 8192 * 96 * 128 * 4
+    assert L.U - L.W >= tok and L.Delta - L.hc >= 257 * 96 * 128 * 128 * 4 and L.total - L.Delta >= tok
+    assert K.lib().kda_fwd_workspace_size(ctypes.byref(d)) == L.total
+    d2 = desc(K, T=100, N=7)       # varlen: ceil(100/32) + 7 slots
+    assert K.lib().kda_staged_layout(ctypes.byref(d2), ctypes.byref(L)) == 0 and L.nslots == 4 + 7
+    assert K.lib().kda_fwd_workspace_size(ctypes.byref(desc(K, Kd=64))) == 0
