@@ -30,6 +30,15 @@ BYTES_PER_TOKEN_HEAD = 3 * 256 + 512 + 4 + 512   # q, k, v bf16 + g fp32 + beta 
 STATE_BYTES = 128 * 128 * 4                        # one (sequence, head) state, fp32
 FLOPS_PER_TOKEN_HEAD = 141013                      # chunked form at C = 64, see the design doc
 
+# Algorithmic bytes of each stage of the staged path (fp32 intermediates,
+# 32-token chunks), per token-head: each tensor read or written once.
+STAGE_BYTES = {
+    "a1_gate_scan": 512 + 512 + 16,                      # g in; Gamma, gamma_last out
+    "a2_intra": 768 + 512 + 4 + 4 * 512 + 128,           # q, k, v, Gamma, beta in; W, U, Kt, Qg, M out
+    "a3_recurrence": 3 * 512 + 16 + 2048 + 512,          # W, U, Kt, gamma_last in; h_c, Delta out
+    "a4_output": 512 + 2048 + 128 + 512 + 512,           # Qg, h_c, M, Delta in; o out
+}
+
 
 def alg_bytes(cfg) -> int:
     per_state = STATE_BYTES * cfg.N * cfg.H
@@ -48,7 +57,7 @@ def kernel_source_hash() -> str:
 def traffic_from_profile(workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
     taken on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", f"kda_fwd_fused_{workload}_counters.md")
+    path = os.path.join(ROOT, "profiles", f"kda_fwd_pipe_{workload}_counters.md")
     if not os.path.exists(path):
         return None
     txt = open(path).read()
@@ -69,6 +78,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--protocol-repeats", type=int, default=5,
                     help="extra repeats of --steps iterations (the pages' 30/200/5 protocol)")
+    ap.add_argument("--path", choices=["fused", "staged"], default="fused",
+                    help="fused: kda_fwd (the hot path); staged: kda_fwd_staged (five kernels)")
+    ap.add_argument("--stages", action="store_true", help="also time each staged-path kernel on its own")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="run one device-to-device copy of this many MiB at the end (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
@@ -96,8 +110,18 @@ def main():
     o = torch.empty((cfg.B, cfg.T, cfg.H, 128), dtype=torch.float32, device=dev)
     hT = torch.empty((cfg.N, cfg.H, 128, 128), dtype=torch.float32, device=dev)
 
-    def step():
-        kda.fwd(q, k, v, g, beta, cu_seqlens=cu, initial_state=h0, out=o, final_state=hT)
+    if args.path == "fused":
+        def step():
+            kda.fwd(q, k, v, g, beta, cu_seqlens=cu, initial_state=h0, out=o, final_state=hT)
+    else:
+        st = kda.Staged(q, k, v, g, beta, cu_seqlens=cu, initial_state=h0)
+
+        def step():
+            st.chunk_map()
+            st.gate_scan()
+            st.intra()
+            st.recurrence(hT)
+            st.output(o)
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -126,6 +150,41 @@ def main():
         b_.record(stream)
         torch.cuda.synchronize()
         reps.append(a_.elapsed_time(b_) / args.steps)
+
+    stage_times = None
+    if args.stages:
+        st = st if args.path == "staged" else kda.Staged(q, k, v, g, beta, cu_seqlens=cu, initial_state=h0)
+        st.chunk_map()
+        st.gate_scan()
+        st.intra()
+        st.recurrence(hT)
+        torch.cuda.synchronize()
+        stage_times = {}
+        for name, fn in (("a0_chunk_map", st.chunk_map), ("a1_gate_scan", st.gate_scan), ("a2_intra", st.intra),
+                         ("a3_recurrence", lambda: st.recurrence(hT)), ("a4_output", lambda: st.output(o))):
+            n_it = max(3, args.steps // 10)
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record(stream)
+            for _ in range(n_it):
+                fn()
+            b_.record(stream)
+            torch.cuda.synchronize()
+            t_ms = a_.elapsed_time(b_) / n_it
+            entry = {"ms": t_ms}
+            if name in STAGE_BYTES:
+                gbs = cfg.token_heads * STAGE_BYTES[name] / (t_ms / 1e3) / 1e9
+                entry.update({"alg_bytes_per_token_head": STAGE_BYTES[name], "achieved_GBs": gbs,
+                              "frac_hbm": gbs / HBM_PEAK_GBS})
+            stage_times[name] = entry
+        log(f"[bench] stages: {stage_times}")
+
+    if args.calib_copy_mb:
+        nbytes = args.calib_copy_mb << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {nbytes} bytes done")
 
     tokens = cfg.B * cfg.T
     value = tokens / (ms / 1e3)
@@ -157,11 +216,15 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "kda_fwd_fused", "alg_bytes_per_launch": bytes_},
+                     "kernel": "kda_fwd_pipe" if (args.path == "fused" and cfg.dtype == "bf16")
+                     else ("kda_fwd_fused (serial)" if args.path == "fused" else "staged path (5 kernels)"),
+                     "alg_bytes_per_launch": bytes_},
         "mfma": {"achieved": flops / (ms / 1e3) / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": flops / (ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
         "protocol": {"repeats": len(reps), "iters": args.steps, "median_ms": float(np.median(reps)) if reps else None,
                      "min_ms": min(reps) if reps else None, "max_ms": max(reps) if reps else None},
+        "path": args.path,
+        "stages": stage_times,
         "wall_s_timed_region": wall,
         "cpu_baseline": cpu,
     }
