@@ -1,20 +1,27 @@
 // kda_fused_pipe.hip -- the pipelined fused chunked KDA forward for gfx950
 // (bf16 q/k/v).
 //
-// Same arithmetic as the serial kernel (kda_fused_serial.hip), organised as a
-// two-stage pipeline inside each workgroup:
+// Same chunk algebra as the serial kernel (kda_fused_serial.hip), organised as
+// a two-stage pipeline inside each workgroup:
 //   * NS "state" waves each own 16 V columns of the 128 x 128 fp32 state of one
 //     (sequence, head) and run only the sequential, MFMA-bound part for chunk i:
 //        P = (K*gamma) S,  Delta = (I + A)^{-1} Diag(beta) (V - P),
 //        O = (Q*gamma) S + M Delta,  S <- Diag(gamma_last) S + Kt^T Delta;
-//   * NH "helper" waves prepare chunk i+1 at the same time: the per-chunk
-//     cumulative log-gate scan, the gated factors, the gated K K^T (A) and
-//     Q K^T (M) blocks on MFMA, and the inverses of the diagonal blocks of
-//     I + A; they write the state waves' operands into the other half of a
+//   * NH "helper" waves prepare chunk i+1 at the same time. A helper lane owns
+//     two channels of four consecutive tokens; one wave holds all eight
+//     segments of its channels, so the in-chunk log-gate scan needs no
+//     workgroup synchronisation. The lane forms every gated factor of its
+//     eight elements; after the mid-chunk barrier the helpers build the
+//     gated K K^T blocks (A, bf16 MFMA), the gated Q K^T blocks (M, fp32
+//     MFMA) and the inverses of the diagonal blocks of I + A (fp32 MFMA),
+//     writing the state waves' operands into the other half of a
 //     double-buffered LDS area.
-// One workgroup barrier per chunk hands the buffers over. The two points where
-// the helpers need each other's results inside a chunk use an LDS counter
-// that only the helpers wait on, so the state waves never stall there.
+// Two workgroup barriers per chunk: one in the middle, where the helpers have
+// finished the factors of chunk i+1 and the state waves the products with the
+// old state of chunk i, and one at the end, which hands the operand buffers
+// over. Two helper waves share each SIMD with one state wave: a single wave
+// issues a VALU instruction at most every other slot, so the helpers' element
+// work needs two waves per SIMD.
 // The split into a chunk-parallel preparation and a sequential recurrence is
 // the pages' two-kernel design (toolarium.ru page, section "Где ограничения
 // прямо сейчас"); here the two run concurrently on one CU so that each input
@@ -27,53 +34,83 @@ namespace pipe {
 
 constexpr int C = 32;          // chunk length (two 16-token sub-blocks)
 constexpr int NS = 4;          // state waves, 16 V columns each
-constexpr int NH = 8;          // helper waves
+constexpr int NH = 8;          // helper waves, 16 channels each
 constexpr int NT = 64 * (NS + NH);
 constexpr int VB = 16 * NS;    // V columns per workgroup
 constexpr int P = D / VB;      // workgroups per (sequence, head)
-constexpr int TS = C / NH;     // tokens per helper segment
-constexpr int LDP = D + 8;     // padded row of a 2-byte [row][128] array
-constexpr int TP = C + 8;      // padded row of a 2-byte [row][32] array
-constexpr int LDA = 16 + 4;    // padded row of an fp32 16 x 16 tile
+constexpr int SEG = 4;         // tokens per helper lane
+constexpr int NSEG = C / SEG;  // segments per chunk (lanes 8*seg + cp)
+constexpr int LDP = D + 8;     // row pitch of a 2-byte [token][channel] array
+constexpr int SHIFT = 16;      // extra 2-byte elements before each further group of eight rows
+constexpr int LD32 = D + 4;    // row pitch of an fp32 [token][channel] array
+constexpr int TP = C + 8;      // row pitch of a 2-byte [row][32] array
 constexpr float LOG2E = 1.4426950408889634f;
+static_assert(NH * 16 == D && NSEG * 8 == 64, "helper lanes: 8 channel pairs x 8 segments per wave");
 
-// 2^x as one v_exp_f32. Every argument here lies within [-60, 60] (log2 units
-// of a 16-token decay span with g >= -5), far from fp32's denormal range, so
-// the library's range handling around the instruction is not needed.
+// Row r of a [token][channel] 2-byte array. Each group of eight rows starts 32
+// bytes further on than the plain pitch would put it: the eight segments of a
+// helper wave, which store the same channel pair of eight rows four apart,
+// then fall on four different bank groups (two writes per bank, the least for
+// 256 bytes), while MFMA operand reads of eight consecutive rows stay
+// conflict-free. An array of R rows holds R * LDP + (R / 8 - 1) * SHIFT.
+__device__ __forceinline__ constexpr int srow(int r) { return r * LDP + (r >> 3) * SHIFT; }
+constexpr int ROWS32 = C * LDP + 3 * SHIFT;
+constexpr int ROWS16 = 16 * LDP + SHIFT;
+
+// 2^x as one v_exp_f32. Every argument here lies within [-120, 60] (log2
+// units of at most 24 decay steps with g >= -5) or underflows harmlessly:
+// such a factor only multiplies a product that is itself below 2^-120.
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
-static_assert(NH * 64 * TS * 2 == C * D, "one (channel pair, segment) per helper thread");
-static_assert(16 % TS == 0 && 8 % TS == 0, "segments must not straddle a sub-block or its middle");
-static_assert(NH == 4 || NH >= 6, "A/M tile assignments exist for four or six-plus helper waves");
+
+// Raw buffer access to one chunk of a [row][H][128] tensor: the resource
+// starts at the chunk's first row (this head) and ends after its last valid
+// row, so reads of rows past the end return zero and writes there are dropped.
+// Word 3 is the gfx9 raw-buffer format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void* p, long long elem_off, int elem_bytes,
+                                                             int nv, uint32_t row_elems, int valid_elems) {
+    const char* base = static_cast<const char*>(p) + elem_off * elem_bytes;
+    const int nbytes = nv > 0 ? ((nv - 1) * (int)row_elems + valid_elems) * elem_bytes : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, nbytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float x0, float x1) {
+    bf16x2 h = {(__bf16)x0, (__bf16)x1};
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// Value of the neighbouring lane (l ^ 1).
+__device__ __forceinline__ float swap_pair(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
 
 // Operands of one chunk for the state waves (double-buffered).
 struct alignas(16) Ops {
-    _Float16 Kg[C][LDP];        // K * exp(Gamma), channels permuted in 32-groups
-    _Float16 Qg[C][LDP];        // Q * exp(Gamma), same order
-    _Float16 KtT[2][D][TP];     // (K * exp(Gamma_last - Gamma))^T, [hi, lo][channel][kperm(token)]
-    _Float16 Tm[C][TP];         // block-diagonal (I + A)^{-1}, [row][kperm(col)]
-    _Float16 A10[16][TP];       // A rows 16-31, cols 0-15, [row][kperm(col)]
-    _Float16 M[2][C][TP];       // lower gated Q K^T, [hi, lo][row][kperm(col)]
-    float gl[D];                // exp(Gamma_last), the chunk's decay per channel
+    _Float16 Kg[ROWS32];            // K * exp(Gamma); channels permuted in 32-groups; rows at srow()
+    _Float16 Qg[ROWS32];            // Q * exp(Gamma), same layout
+    _Float16 KtT[D][TP];            // (K * exp(Gamma_last - Gamma))^T, [channel][kperm(token)]
+    _Float16 Tm[C][TP];             // block-diagonal (I + A)^{-1}, [row][kperm(col)]
+    _Float16 A10[16][TP];           // A rows 16-31, cols 0-15, [row][kperm(col)]
+    _Float16 M[2][C][TP];           // lower gated Q K^T, [hi, lo][row][kperm(col)]
+    float gl[D];                    // exp(Gamma_last), the chunk's decay per channel
     float beta[C];
 };
 
 struct alignas(16) Smem {
     Ops op[2];
-    __bf16 Ka[C][LDP];          // k * exp(Gamma_r - Gamma_mid(block)) (A needs only bf16)
-    __bf16 Qa[2][C][LDP];       // q * exp(Gamma_r - Gamma_mid(block))
-    __bf16 Kb[2][C][LDP];       // k * exp(Gamma_mid(block) - Gamma_r)
-    __bf16 Kr[2][16][LDP];      // block-0 keys referenced to block 1's middle
-    float Ad[2][16][LDA];       // diagonal blocks of A for the forward substitution
-    float qtot[NH][D];          // sum of g * log2(e) over each helper segment
-    uint32_t hcount;            // helper-only barrier counter
+    __bf16 Ka[ROWS32];              // k * exp(Gamma_r - Gamma_mid(block)), rows at srow()
+    __bf16 Kb[ROWS32];              // k * exp(Gamma_mid(block) - Gamma_r)
+    __bf16 Kr[ROWS16];              // block-0 keys referenced to block 1's middle
+    float Qa[C][LD32];              // q * exp(Gamma_r - Gamma_mid(block)), fp32 for M
+    float Kb32[C][LD32];            // Kb in fp32 for M
+    float Kr32[16][LD32];           // Kr in fp32 for M
+    float2 segsum[NH][8][NSEG];     // per helper wave: segment sums of each channel pair
+    f32x4 mpart[64];                // half of the M11 block, handed from one helper wave to another
+    uint32_t pcount;                // hand-over counter of mpart
 };
 
-// Helper-only barrier: an LDS counter that every helper wave bumps and then
-// waits on. The wait is bounded; under correct use it never runs out.
-__device__ __forceinline__ void helper_sync(uint32_t* cnt, uint32_t& target, int lane) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    if (lane == 0) __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    target += NH;
+// Waits until an LDS counter reaches target. The wait is bounded; under
+// correct use it never runs out.
+__device__ __forceinline__ void wait_count(const uint32_t* cnt, uint32_t target) {
     for (uint32_t spin = 0; spin < (1u << 20); ++spin) {
         if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
         __builtin_amdgcn_s_sleep(1);
@@ -85,239 +122,267 @@ __device__ __forceinline__ float2 bf2(uint32_t u) {
     return make_float2(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
 }
 
-// One helper thread's share of a chunk: channels 2cp, 2cp+1 of tokens seg*TS .. +TS.
-// Loads are unconditional from a clamped (valid) token so that no load sits
-// behind a branch that would make the compiler wait for it on the spot;
-// tokens past the chunk's end are zeroed where the values are used.
+// One helper lane's inputs of a chunk: channels 2cp, 2cp+1 (of its wave's 16)
+// of tokens 4seg .. 4seg+3, and beta of one token. Tokens past the chunk's end
+// read as zero (see chunk_rsrc), which makes their gate, key and query vanish
+// from every product.
 struct HFetch {
-    float2 g[TS];
-    uint32_t k[TS], q[TS];
+    float2 g[SEG];
+    uint32_t k[SEG], q[SEG];
     float beta;
+};
+// Byte offsets of those elements within a chunk of k or q, of g, and of beta.
+struct HOffs {
+    uint32_t kq[SEG], gg[SEG], b;
 };
 
 __device__ __forceinline__ void hfetch(HFetch& f, const FwdArgs& a, long long cbase, long long cbeta,
-                                       uint32_t ts, uint32_t off0, int nv, int seg, int ht) {
-    const uint16_t* kp = static_cast<const uint16_t*>(a.k) + cbase;
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + cbase;
-    const float* gp = a.g + cbase;
+                                       uint32_t ts, int nv, const HOffs& off) {
+    const auto rk = chunk_rsrc(a.k, cbase, 2, nv, ts, D);
+    const auto rq = chunk_rsrc(a.q, cbase, 2, nv, ts, D);
+    const auto rg = chunk_rsrc(a.g, cbase, 4, nv, ts, D);
+    const auto rb = chunk_rsrc(a.beta, cbeta, 4, nv, (uint32_t)a.H, 1);
 #pragma unroll
-    for (int t = 0; t < TS; ++t) {
-        const int rc = min(seg * TS + t, nv - 1);
-        const uint32_t o = off0 + (uint32_t)rc * ts;
-        f.g[t] = *reinterpret_cast<const float2*>(gp + o);
-        f.k[t] = *reinterpret_cast<const uint32_t*>(kp + o);
-        f.q[t] = *reinterpret_cast<const uint32_t*>(qp + o);
+    for (int t = 0; t < SEG; ++t) {
+        f.g[t] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rg, off.gg[t], 0, 0));
+        f.k[t] = __builtin_amdgcn_raw_buffer_load_b32(rk, off.kq[t], 0, 0);
+        f.q[t] = __builtin_amdgcn_raw_buffer_load_b32(rq, off.kq[t], 0, 0);
     }
-    f.beta = a.beta[cbeta + (uint32_t)min(ht, nv - 1) * (uint32_t)a.H];
+    f.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, off.b, 0, 0));
 }
 
-// Forward substitution of one unit-lower-triangular 16 x 16 block: lane j
-// (of 16) returns column j of (I + Ablk)^{-1}. The lower triangle is read into
-// registers first (36 broadcast 16-byte reads), so the 16 dependent row steps
-// wait on FMAs only, not on LDS round trips.
-__device__ __forceinline__ void tri_inverse16(const float (*Ablk)[LDA], int j, float x[16]) {
-    float4 ar[16][4];
-#pragma unroll
-    for (int r = 1; r < 16; ++r)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            if (4 * q < r) ar[r][q] = *reinterpret_cast<const float4*>(&Ablk[r][4 * q]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        float s0 = (r == j) ? 1.f : 0.f, s1 = 0.f;
-#pragma unroll
-        for (int i = 0; i < r; ++i) {
-            const float4 v4 = ar[r][i >> 2];
-            const float av = (i & 3) == 0 ? v4.x : (i & 3) == 1 ? v4.y : (i & 3) == 2 ? v4.z : v4.w;
-            if (i & 1) s1 -= av * x[i];
-            else s0 -= av * x[i];
-        }
-        x[r] = s0 + s1;
-    }
-}
+// Helpers, step 1: the gated factors of one chunk from the fetched registers,
+// then the fetch of the chunk after it into the same registers.
+//
+// In-chunk cumulative log-gate Gamma, per channel, from the eight segment sums
+// S0..S7 (segments 0-3 form sub-block 0, segments 4-7 sub-block 1). Factors
+// are referenced to the middle of their sub-block (Gamma at its token 7):
+// S0+S1 for sub-block 0 and tau0+S4+S5 for sub-block 1 (tau0 = S0+..+S3), so
+// each stays within exp(+-40) for g >= -5.
+__device__ __forceinline__ void factors(Smem& sm, Ops& op, HFetch& f, int hw, int lane,
+                                        bool fetch_next, const FwdArgs& a, long long nbase, long long nbeta,
+                                        uint32_t ts, const HOffs& offs, int nnv) {
+    const int cp = lane & 7, seg = lane >> 3;
+    const int b = seg >> 2;
+    const int c0 = 16 * hw + 2 * cp;
 
-// Helpers: prepare the operands of one chunk from the fetched registers.
-__device__ __forceinline__ void prepare(Smem& sm, Ops& op, HFetch& f, int nv, int hw, int lane,
-                                        int ht, uint32_t& htarget, bool fetch_next,
-                                        const FwdArgs& a, long long nbase, long long nbeta, uint32_t ts,
-                                        uint32_t off, int nnv) {
-    const int cp = ht & 63, seg = ht >> 6;
-    const int b = (seg * TS) >> 4;                 // sub-block of this segment
-    const int l16 = lane & 15, grp = lane >> 4;
-
-    // (1a) local scan in log2 units
-    float L[2][TS];
-    float kv[2][TS], qv[2][TS];
-    {
-        float r0 = 0.f, r1 = 0.f;
+    float L[2][SEG], kv[2][SEG], qv[2][SEG];
+    float r0 = 0.f, r1 = 0.f;
 #pragma unroll
-        for (int t = 0; t < TS; ++t) {
-            const bool ok = seg * TS + t < nv;
-            r0 += ok ? f.g[t].x * LOG2E : 0.f;
-            r1 += ok ? f.g[t].y * LOG2E : 0.f;
-            L[0][t] = r0;
-            L[1][t] = r1;
-            const float2 k2 = bf2(ok ? f.k[t] : 0u), q2 = bf2(ok ? f.q[t] : 0u);
-            kv[0][t] = k2.x; kv[1][t] = k2.y;
-            qv[0][t] = q2.x; qv[1][t] = q2.y;
-        }
-        *reinterpret_cast<float2*>(&sm.qtot[seg][2 * cp]) = make_float2(r0, r1);
+    for (int t = 0; t < SEG; ++t) {
+        r0 += f.g[t].x;
+        r1 += f.g[t].y;
+        L[0][t] = r0;
+        L[1][t] = r1;
+        const float2 k2 = bf2(f.k[t]), q2 = bf2(f.q[t]);
+        kv[0][t] = k2.x; kv[1][t] = k2.y;
+        qv[0][t] = q2.x; qv[1][t] = q2.y;
     }
-    if (ht < C) op.beta[ht] = (ht < nv) ? f.beta : 0.f;
-    helper_sync(&sm.hcount, htarget, lane);
+    sm.segsum[hw][cp][seg] = make_float2(r0, r1);
+    if (hw == 0 && cp < SEG) op.beta[SEG * seg + cp] = f.beta;
     // the fetched registers are consumed: fetch the chunk after this one
-    if (fetch_next) hfetch(f, a, nbase, nbeta, ts, off, nnv, seg, ht);
+    if (fetch_next) hfetch(f, a, nbase, nbeta, ts, nnv, offs);
 
-    // (1b) gated factors
-    {
-        constexpr int SPB = 16 / TS;               // segments per sub-block
-        constexpr int MIDSEG = 8 / TS - 1;         // last segment of a sub-block's first half
-        float d[2][TS], c1[2], c2[2], c3[2];
+    // all eight segment sums of this channel pair (written by this wave)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float St[2][NSEG];
+#pragma unroll
+    for (int s = 0; s < NSEG; s += 2) {
+        const float4 v = lds_vec<float4>(&sm.segsum[hw][cp][s]);
+        St[0][s] = v.x; St[1][s] = v.y; St[0][s + 1] = v.z; St[1][s + 1] = v.w;
+    }
+    float d[2][SEG], c1[2], c2[2], c3[2];
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) {
+        const float* S = St[ch];
+        const float tau0 = S[0] + S[1] + S[2] + S[3];
+        const float tau1 = S[4] + S[5] + S[6] + S[7];
+        const float rho0 = S[0] + S[1], rho1 = S[4] + S[5];   // block-local middles
+        // sum of the earlier segments of this lane's sub-block
+        float pre = 0.f;
+#pragma unroll
+        for (int s = 0; s < NSEG - 1; ++s)
+            if (s < seg && (s >> 2) == b) pre += S[s];
+        const float rho = b ? rho1 : rho0;
+        c1[ch] = ex2((b ? tau0 + rho1 : rho0) * LOG2E);                 // exp(Gamma_mid)              -> K*gamma, Q*gamma
+        c2[ch] = ex2((b ? tau1 - rho1 : tau0 + tau1 - rho0) * LOG2E);   // exp(Gamma_last - Gamma_mid) -> Kt
+        c3[ch] = ex2((tau0 + rho1 - rho0) * LOG2E);                     // block 0 -> block 1's middle -> Kr
+        const float moff = (pre - rho) * LOG2E;
+#pragma unroll
+        for (int t = 0; t < SEG; ++t) d[ch][t] = fmaf(L[ch][t], LOG2E, moff);
+    }
+    if (seg == 0) *reinterpret_cast<float2*>(&op.gl[c0]) = make_float2(c1[0] * c2[0], c1[1] * c2[1]);
+
+    const int cpos = (c0 & ~31) | kperm(c0 & 31);
+    float kt[2][SEG];
+#pragma unroll
+    for (int t = 0; t < SEG; ++t) {
+        const int r = SEG * seg + t;
+        const int so = srow(r);
+        float ka[2], qa[2], kb[2], kr[2];
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
-            const int c = 2 * cp + ch;
-            float tot0 = 0.f, tot1 = 0.f, L7b0 = 0.f, L7b1 = 0.f, pre = 0.f;
-#pragma unroll
-            for (int s = 0; s < NH; ++s) {
-                const float v = sm.qtot[s][c];
-                if (s < SPB) { tot0 += v; if (s <= MIDSEG) L7b0 += v; }
-                else { tot1 += v; if (s - SPB <= MIDSEG) L7b1 += v; }
-                if (s < seg && s >= b * SPB) pre += v;      // earlier segments of this sub-block
-            }
-            const float L7 = b ? L7b1 : L7b0;
-            const float L15 = b ? tot1 : tot0;
-            const float start = b ? tot0 : 0.f;
-            const float after = b ? 0.f : tot1;
-            c1[ch] = ex2(start + L7);                // exp(Gamma_mid)              -> K*gamma, Q*gamma
-            c2[ch] = ex2(L15 - L7 + after);          // exp(Gamma_last - Gamma_mid) -> Kt
-            c3[ch] = ex2(L15 - L7 + L7b1);           // block 0 -> block 1's middle -> Kr
-            if (seg == 0) op.gl[c] = ex2(tot0 + tot1);
-#pragma unroll
-            for (int t = 0; t < TS; ++t) d[ch][t] = L[ch][t] + pre - L7;
+            const float e1 = ex2(d[ch][t]), e2 = ex2(-d[ch][t]);
+            ka[ch] = kv[ch][t] * e1;
+            qa[ch] = qv[ch][t] * e1;
+            kb[ch] = kv[ch][t] * e2;
+            kt[ch][t] = kb[ch] * c2[ch];
+            kr[ch] = kb[ch] * c3[ch];
         }
-        const int cpos = ((2 * cp) & ~31) | kperm((2 * cp) & 31);
-        float ktp[TS], ktq[TS];
-#pragma unroll
-        for (int t = 0; t < TS; t += 2) {
-            float kt[2][2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int rr = seg * TS + t + u;
-                float ka[2], qa[2], kb[2];
-#pragma unroll
-                for (int ch = 0; ch < 2; ++ch) {
-                    const float e1 = ex2(d[ch][t + u]), e2 = ex2(-d[ch][t + u]);
-                    ka[ch] = kv[ch][t + u] * e1;
-                    qa[ch] = qv[ch][t + u] * e1;
-                    kb[ch] = kv[ch][t + u] * e2;
-                    kt[u][ch] = kb[ch] * c2[ch];
-                }
-                uint32_t hi, lo;
-                {
-                    const bf16x2 kah = {(__bf16)ka[0], (__bf16)ka[1]};
-                    *reinterpret_cast<bf16x2*>(&sm.Ka[rr][2 * cp]) = kah;
-                }
-                split_bf16x2(qa[0], qa[1], hi, lo);
-                *reinterpret_cast<uint32_t*>(&sm.Qa[0][rr][2 * cp]) = hi;
-                *reinterpret_cast<uint32_t*>(&sm.Qa[1][rr][2 * cp]) = lo;
-                split_bf16x2(kb[0], kb[1], hi, lo);
-                *reinterpret_cast<uint32_t*>(&sm.Kb[0][rr][2 * cp]) = hi;
-                *reinterpret_cast<uint32_t*>(&sm.Kb[1][rr][2 * cp]) = lo;
-                if (b == 0) {
-                    split_bf16x2(kb[0] * c3[0], kb[1] * c3[1], hi, lo);
-                    *reinterpret_cast<uint32_t*>(&sm.Kr[0][rr][2 * cp]) = hi;
-                    *reinterpret_cast<uint32_t*>(&sm.Kr[1][rr][2 * cp]) = lo;
-                }
-                *reinterpret_cast<uint32_t*>(&op.Kg[rr][cpos]) = pack_f16(ka[0] * c1[0], ka[1] * c1[1]);
-                *reinterpret_cast<uint32_t*>(&op.Qg[rr][cpos]) = pack_f16(qa[0] * c1[0], qa[1] * c1[1]);
-            }
-            // K^T: tokens come in pairs here and in quads below
-            ktp[t] = kt[0][0]; ktp[t + 1] = kt[1][0];
-            ktq[t] = kt[0][1]; ktq[t + 1] = kt[1][1];
+        *reinterpret_cast<uint32_t*>(&sm.Ka[so + c0]) = pack_bf16(ka[0], ka[1]);
+        *reinterpret_cast<uint32_t*>(&sm.Kb[so + c0]) = pack_bf16(kb[0], kb[1]);
+        *reinterpret_cast<float2*>(&sm.Qa[r][c0]) = make_float2(qa[0], qa[1]);
+        *reinterpret_cast<float2*>(&sm.Kb32[r][c0]) = make_float2(kb[0], kb[1]);
+        if (b == 0) {
+            *reinterpret_cast<uint32_t*>(&sm.Kr[so + c0]) = pack_bf16(kr[0], kr[1]);
+            *reinterpret_cast<float2*>(&sm.Kr32[r][c0]) = make_float2(kr[0], kr[1]);
         }
-        // tokens seg*TS .. seg*TS+3 occupy four contiguous kperm positions: 8-byte stores
-        static_assert(TS == 4, "the K^T store below writes one 4-token group per channel");
-        const int tp = kperm(seg * TS);
+        *reinterpret_cast<uint32_t*>(&op.Kg[so + cpos]) = pack_f16(ka[0] * c1[0], ka[1] * c1[1]);
+        *reinterpret_cast<uint32_t*>(&op.Qg[so + cpos]) = pack_f16(qa[0] * c1[0], qa[1] * c1[1]);
+    }
+    // K~^T: the lane's four tokens are four consecutive kperm positions
+    const int tp = kperm(SEG * seg);
 #pragma unroll
-        for (int ch = 0; ch < 2; ++ch) {
-            const float* kq = ch ? ktq : ktp;
-            uint32_t h01, l01, h23, l23;
-            split_f16x2(kq[0], kq[1], h01, l01);
-            split_f16x2(kq[2], kq[3], h23, l23);
-            *reinterpret_cast<uint2*>(&op.KtT[0][2 * cp + ch][tp]) = make_uint2(h01, h23);
-            *reinterpret_cast<uint2*>(&op.KtT[1][2 * cp + ch][tp]) = make_uint2(l01, l23);
+    for (int ch = 0; ch < 2; ++ch)
+        *reinterpret_cast<uint2*>(&op.KtT[c0 + ch][tp]) =
+            make_uint2(pack_f16(kt[ch][0], kt[ch][1]), pack_f16(kt[ch][2], kt[ch][3]));
+}
+
+// 16 x 16 block of M on fp32 MFMA: rows from Qa (tokens qr..qr+15), columns
+// from B32 (tokens 0..15 of that array). K-slot g of the four products taken
+// from one 16-byte read is channel 16*mq + 4*g + (0..3); channels 16*MQ0 up
+// to 16*MQ1 are summed.
+template <int MQ0 = 0, int MQ1 = D / 16>
+__device__ __forceinline__ f32x4 mtile(const float (*Qa)[LD32], const float (*B32)[LD32], int qr, int l16, int grp) {
+    f32x4 m0 = {0.f, 0.f, 0.f, 0.f}, m1 = m0;
+#pragma unroll
+    for (int mq = MQ0; mq < MQ1; ++mq) {
+        const float4 qa = lds_vec<float4>(&Qa[qr + l16][16 * mq + 4 * grp]);
+        const float4 kb = lds_vec<float4>(&B32[l16][16 * mq + 4 * grp]);
+        m0 = mfma16x4(qa.x, kb.x, m0);
+        m1 = mfma16x4(qa.y, kb.y, m1);
+        m0 = mfma16x4(qa.z, kb.z, m0);
+        m1 = mfma16x4(qa.w, kb.w, m1);
+    }
+    return m0 + m1;
+}
+
+// X Y for 16 x 16 fp32 matrices on fp32 MFMA, from X^T and Y in accumulator
+// layout (lane: rows 4grp+j, column l16), into the same layout, added to c.
+// Product m pairs K-slot g with index 4g + m, which is register j = m of both
+// operands.
+__device__ __forceinline__ f32x4 mprod(const f32x4& xt, const f32x4& y, f32x4 c) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) c = mfma16x4(xt[m], y[m], c);
+    return c;
+}
+
+// Stores a 16 x 16 accumulator tile (lane: rows 4grp+j, column l16) into a
+// [row][kperm(col)] fp16 array as 32-bit pairs of adjacent columns: the two
+// lanes of a column pair swap half their rows, so an even lane writes rows j
+// = 0, 2 and an odd lane rows 1, 3. With two arrays (hi, lo) the value is
+// stored as a two-term split. Diagonal tiles keep col <= row.
+template <bool SPLIT>
+__device__ __forceinline__ void store_tile(_Float16 (*hi)[TP], _Float16 (*lo)[TP], const f32x4& m, int r0, int c0,
+                                           bool diag, int l16, int grp) {
+    const bool odd = l16 & 1;
+    float mine[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = 4 * grp + j;
+        mine[j] = (!diag || l16 <= r) ? m[j] : 0.f;
+    }
+    // send the rows the partner writes: even lanes send rows 1, 3; odd lanes rows 0, 2
+    const float got0 = swap_pair(odd ? mine[0] : mine[1]);
+    const float got1 = swap_pair(odd ? mine[2] : mine[3]);
+    const int cpos = kperm(c0 + (l16 & ~1));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int j = 2 * h + (odd ? 1 : 0);
+        const float own = odd ? (h ? mine[3] : mine[1]) : (h ? mine[2] : mine[0]);
+        const float oth = h ? got1 : got0;
+        const float x0 = odd ? oth : own, x1 = odd ? own : oth;   // columns c0 + 2a, c0 + 2a + 1
+        const int r = r0 + 4 * grp + j;
+        if constexpr (SPLIT) {
+            uint32_t wh, wl;
+            split_f16x2(x0, x1, wh, wl);
+            *reinterpret_cast<uint32_t*>(&hi[r][cpos]) = wh;
+            *reinterpret_cast<uint32_t*>(&lo[r][cpos]) = wl;
+        } else {
+            *reinterpret_cast<uint32_t*>(&hi[r][cpos]) = pack_f16(x0, x1);
         }
     }
-    helper_sync(&sm.hcount, htarget, lane);
+}
 
-    // (2) A and M blocks on MFMA; the diagonal blocks of A are inverted by the
-    // wave that built them.
-    //   six or more helpers:  hw 0: A00 -> T00  1: A11 -> T11  2: A10  3: M10  4: M00  5: M11
-    //   four helpers:         hw 0: A00 -> T00  1: A11 -> T11  2: A10, M10    3: M00, M11
-    constexpr int NTILE = (NH >= 6) ? 1 : 2;
-    for (int ti = 0; ti < NTILE; ++ti) {
-        int tile;                                  // 0 A00, 1 A11, 2 A10, 3 M10, 4 M00, 5 M11
-        if constexpr (NH >= 6) tile = hw;
-        else tile = (hw < 2) ? (ti == 0 ? hw : 6) : (hw == 2 ? 2 + ti : 4 + ti);
-        if (tile >= 6) continue;
-        const bool isM = tile >= 3;
-        const int rb = (tile == 0 || tile == 4) ? 0 : 1;
-        const int cb = (tile == 2 || tile == 3) ? 0 : rb;
-        const bool diag = (rb == cb);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = acc, acc3 = acc;
+// Helpers, step 2: A and M blocks, and the inverses of the diagonal blocks.
+//   hw 0: A00 -> T00   hw 1: A11 -> T11   hw 2: M00   hw 3: M10   hw 4: A10
+//   hw 6, 7: M11, half of the channels each
+// An M block is 32 fp32 MFMAs, as is the inverse of a diagonal block of I + A;
+// helper wave hw shares SIMD hw % 4 with the other helper and one state wave,
+// so this spreads the fp32 products evenly over the four matrix cores.
+// The zero blocks of Tm, A10 and M are written once, at the kernel's start.
+__device__ __forceinline__ void tiles(Smem& sm, Ops& op, int hw, int lane, uint32_t ptarget) {
+    const int l16 = lane & 15, grp = lane >> 4;
+    if (hw <= 1) {
+        // A_bb and its transpose (the same products with the operands swapped)
+        const int rb = hw;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acct = acc;
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
-            const int off32 = 32 * kk + 8 * grp;
-            const int rrow = 16 * rb + l16;
-            const bf16x8 ch = lds_vec<bf16x8>(diag ? &sm.Kb[0][16 * cb + l16][off32] : &sm.Kr[0][l16][off32]);
-            if (isM) {   // M feeds the output directly: two-term split on both sides
-                const bf16x8 rh = lds_vec<bf16x8>(&sm.Qa[0][rrow][off32]);
-                const bf16x8 rl = lds_vec<bf16x8>(&sm.Qa[1][rrow][off32]);
-                const bf16x8 cl = lds_vec<bf16x8>(diag ? &sm.Kb[1][16 * cb + l16][off32] : &sm.Kr[1][l16][off32]);
-                acc = mfma16(rh, ch, acc);      // three independent chains
-                acc2 = mfma16(rh, cl, acc2);
-                acc3 = mfma16(rl, ch, acc3);
-            } else {     // A only conditions the solve: bf16 operands
-                acc = mfma16(lds_vec<bf16x8>(&sm.Ka[rrow][off32]), ch, acc);
-            }
+            const int off = srow(16 * rb + l16) + 32 * kk + 8 * grp;
+            const bf16x8 ka = lds_vec<bf16x8>(&sm.Ka[off]), kb = lds_vec<bf16x8>(&sm.Kb[off]);
+            acc = mfma16(ka, kb, acc);
+            acct = mfma16(kb, ka, acct);
         }
-        if (isM) {
-            acc += acc2 + acc3;
+        // A[r][i] = beta_r (Ka_r . Kb_i) for i < r: lane holds column i = l16 of rows r = 4grp + j,
+        // and A^T: column r = l16 of rows i = 4grp + j.
+        const float bcol = op.beta[16 * rb + l16];
+        f32x4 A, At, ImA;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 16 * rb + 4 * grp + j, i = 16 * cb + l16;
-                const float val = (i <= r) ? acc[j] : 0.f;
-                split16(val, op.M[0][r][kperm(i)], op.M[1][r][kperm(i)]);
-                if (rb == 0) {
-                    op.M[0][r][kperm(16 + l16)] = (_Float16)0.f;
-                    op.M[1][r][kperm(16 + l16)] = (_Float16)0.f;
-                }
-            }
-        } else if (!diag) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 4 * grp + j;
-                op.A10[r][kperm(l16)] = (_Float16)(op.beta[16 + r] * acc[j]);
-                op.A10[r][kperm(16 + l16)] = (_Float16)0.f;
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 4 * grp + j;
-                sm.Ad[rb][r][l16] = (l16 < r) ? op.beta[16 * rb + r] * acc[j] : 0.f;
-            }
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            float x[16];
-            tri_inverse16(sm.Ad[rb], l16, x);
-            if (grp == 0) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    op.Tm[16 * rb + r][kperm(16 * rb + l16)] = (_Float16)x[r];
-                    op.Tm[16 * rb + r][kperm(16 * (1 - rb) + l16)] = (_Float16)0.f;
-                }
-            }
+        for (int j = 0; j < 4; ++j) {
+            const int r = 4 * grp + j;
+            A[j] = (l16 < r) ? op.beta[16 * rb + r] * acc[j] : 0.f;
+            At[j] = (l16 > r) ? bcol * acct[j] : 0.f;
+            ImA[j] = (l16 == r ? 1.f : 0.f) - A[j];
         }
+        // (I + A)^{-1} = (I - A)(I + A^2)(I + A^4)(I + A^8): A is strictly
+        // lower triangular, so A^16 = 0 and the product is the whole Neumann
+        // series (the factors commute).
+        const f32x4 Z = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 A2 = mprod(At, A, Z), A2t = mprod(A, At, Z);
+        const f32x4 Q1 = mprod(A2t, ImA, ImA);               // (I + A^2)(I - A)
+        const f32x4 A4 = mprod(A2t, A2, Z), A4t = mprod(A2, A2t, Z);
+        const f32x4 Q2 = mprod(A4t, Q1, Q1);                 // (I + A^4) Q1
+        const f32x4 A8t = mprod(A4, A4t, Z);
+        const f32x4 Tb = mprod(A8t, Q2, Q2);                 // (I + A^8) Q2
+        store_tile<false>(op.Tm, nullptr, Tb, 16 * rb, 16 * rb, false, l16, grp);
+    } else if (hw == 4) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) {
+            const int off = 32 * kk + 8 * grp;
+            acc = mfma16(lds_vec<bf16x8>(&sm.Ka[srow(16 + l16) + off]), lds_vec<bf16x8>(&sm.Kr[srow(l16) + off]), acc);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] *= op.beta[16 + 4 * grp + j];
+        store_tile<false>(op.A10, nullptr, acc, 0, 0, false, l16, grp);
+    } else if (hw == 2) {
+        store_tile<true>(op.M[0], op.M[1], mtile(sm.Qa, sm.Kb32, 0, l16, grp), 0, 0, true, l16, grp);
+    } else if (hw == 3) {
+        store_tile<true>(op.M[0], op.M[1], mtile(sm.Qa, sm.Kr32, 16, l16, grp), 16, 0, false, l16, grp);
+    } else if (hw == 6) {
+        // channels 0-63 of M11, handed to hw 7
+        sm.mpart[lane] = mtile<0, D / 32>(&sm.Qa[16], &sm.Kb32[16], 0, l16, grp);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        if (lane == 0) __hip_atomic_fetch_add(&sm.pcount, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    } else if (hw == 7) {
+        // channels 64-127 of M11, plus hw 6's half
+        f32x4 m = mtile<D / 32, D / 16>(&sm.Qa[16], &sm.Kb32[16], 0, l16, grp);
+        wait_count(&sm.pcount, ptarget);
+        m += sm.mpart[lane];
+        store_tile<true>(op.M[0], op.M[1], m, 16, 16, true, l16, grp);
     }
 }
 
@@ -327,6 +392,8 @@ __global__ __launch_bounds__(NT, 1) void kda_fwd_pipe(FwdArgs a) {
     const int l16 = lane & 15, grp = lane >> 4;
     const bool is_state = wave < NS;
 
+    // The P V-blocks of a (sequence, head) sit eight workgroups apart, so they
+    // land on the same XCD and share its L2 for q, k and g.
     const int bid = blockIdx.x;
     const int xcd = bid & 7, rest = bid >> 3;
     const int vblk = rest % P;
@@ -342,155 +409,145 @@ __global__ __launch_bounds__(NT, 1) void kda_fwd_pipe(FwdArgs a) {
     const long long bbase = (long long)row * a.T * a.H + h;
     const long long sbase = ((long long)n * a.H + h) * D * D;
 
-    if (tid == 0) sm.hcount = 0u;
+    // Zero blocks of both operand buffers, never written afterwards: kperm
+    // positions 16-31 of rows 0-15 in Tm, M (hi, lo) and A10, and positions
+    // 0-15 of rows 16-31 in Tm.
+    if (tid == 0) sm.pcount = 0u;
+    for (int i = tid; i < 2 * C * 8; i += NT) {
+        const int bsel = i / (C * 8), r = (i / 8) % C, c = 2 * (i % 8);
+        const int col = kperm((r < 16 ? 16 : 0) + c);
+        Ops& op = sm.op[bsel];
+        *reinterpret_cast<uint32_t*>(&op.Tm[r][col]) = 0u;
+        if (r < 16) {
+            *reinterpret_cast<uint32_t*>(&op.M[0][r][col]) = 0u;
+            *reinterpret_cast<uint32_t*>(&op.M[1][r][col]) = 0u;
+            *reinterpret_cast<uint32_t*>(&op.A10[r][col]) = 0u;
+        }
+    }
     __syncthreads();
 
-    // ---------------- state-wave registers
-    const int vc = vblk * VB + wave * 16 + l16;                     // state lane's V column
-    const uint32_t vofs = (uint32_t)(4 * grp) * ts + vc;            // (row 4grp, column vc) in a chunk
-    f32x4 S[8];
-    uint32_t vcur[8], vnxt[8];
-    // ---------------- helper registers
-    const int ht = tid - 64 * NS, hw = wave - NS;
-    const uint32_t hoff = 2 * (ht & 63);                           // channel pair offset
-    uint32_t htarget = 0;
-    HFetch f;
-
-    // V of this lane's column for the chunk's tokens 16t + 4grp + j, as raw bf16
-    // bits from clamped rows; converted and masked where used.
-    auto vfetch = [&](uint32_t* dst, int cidx) {
-        const int cs = t0 + cidx * C;
-        const int nv = min(C, t1 - cs);
-        const uint16_t* vp = static_cast<const uint16_t*>(a.v) + base + (long long)cs * ts;
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int rc = min(16 * t + 4 * grp + j, nv - 1);
-                dst[4 * t + j] = vp[(uint32_t)rc * ts + vc];
-            }
-    };
-
-    // Both roles execute the same number of workgroup barriers: two before the
-    // chunk loop and one per chunk.
+    // Both roles execute the same number of workgroup barriers: two or three
+    // before the chunk loop and two per chunk.
     if (is_state) {
+        const int vc = vblk * VB + wave * 16 + l16;                     // this lane's V column
+        // byte offsets of (row 16t + 4grp + j, column vc) within a chunk of v (bf16)
+        uint32_t voff[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) voff[i] = ((uint32_t)(16 * (i >> 2) + 4 * grp + (i & 3)) * ts + vc) * 2u;
+        f32x4 S[8];
+        uint32_t vcur[8], vnxt[8];
+        // V of this lane's column for the chunk's tokens 16t + 4grp + j, as raw
+        // bf16 bits (zero past the chunk's end).
+        auto vfetch = [&](uint32_t* dst, int cidx) {
+            const int cs = t0 + cidx * C;
+            const auto rv = chunk_rsrc(a.v, base + (long long)cs * ts, 2, min(C, t1 - cs), ts, D);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) dst[i] = __builtin_amdgcn_raw_buffer_load_b16(rv, voff[i], 0, 0);
+        };
 #pragma unroll
         for (int m = 0; m < 8; ++m)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 S[m][j] = a.h0 ? a.h0[sbase + (uint32_t)(16 * m + 4 * grp + j) * D + vc] : 0.f;
-        if (nch > 0) vfetch(vcur, 0);
+        if (nch > 0) {
+            vfetch(vcur, 0);
+            __syncthreads();   // the helpers' mid-chunk barrier of chunk 0
+        }
         __syncthreads();
         for (int ci = 0; ci < nch; ++ci) {
             const int cs = t0 + ci * C;
             const int nv = min(C, t1 - cs);
-                const Ops& op = sm.op[ci & 1];
-                if (ci + 1 < nch) vfetch(vnxt, ci + 1);
-                f16x8 SBh[4];
+            const Ops& op = sm.op[ci & 1];
+            if (ci + 1 < nch) vfetch(vnxt, ci + 1);
+            // the state as a B operand: rows in kperm order, rounded to fp16
+            f16x8 SBh[4];
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
+            for (int kk = 0; kk < 4; ++kk) {
+                uint32_t w[4];
+                w[0] = pack_f16(S[2 * kk][0], S[2 * kk][1]);
+                w[1] = pack_f16(S[2 * kk][2], S[2 * kk][3]);
+                w[2] = pack_f16(S[2 * kk + 1][0], S[2 * kk + 1][1]);
+                w[3] = pack_f16(S[2 * kk + 1][2], S[2 * kk + 1][3]);
+                SBh[kk] = __builtin_bit_cast(f16x8, w);
+            }
+            f32x4 Pt[2], Ot[2];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        SBh[kk][j] = (_Float16)S[2 * kk][j];
-                        SBh[kk][4 + j] = (_Float16)S[2 * kk + 1][j];
-                    }
-                f32x4 Pt[2], Ot[2];
+            for (int t = 0; t < 2; ++t) {
+                Pt[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                Ot[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    Pt[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    Ot[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) {
-                        const int off = 32 * kk + 8 * grp;
-                        Pt[t] = mfma16(lds_vec<f16x8>(&op.Kg[16 * t + l16][off]), SBh[kk], Pt[t]);
-                        Ot[t] = mfma16(lds_vec<f16x8>(&op.Qg[16 * t + l16][off]), SBh[kk], Ot[t]);
-                    }
+                for (int kk = 0; kk < 4; ++kk) {
+                    const int off = srow(16 * t + l16) + 32 * kk + 8 * grp;
+                    Pt[t] = mfma16(lds_vec<f16x8>(&op.Kg[off]), SBh[kk], Pt[t]);
+                    Ot[t] = mfma16(lds_vec<f16x8>(&op.Qg[off]), SBh[kk], Ot[t]);
                 }
-                float be[2][4];
+            }
+            __syncthreads();   // mid-chunk: the helpers' factors of chunk ci+1 are written
+            float be[2][4];
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        be[t][j] = op.beta[16 * t + 4 * grp + j] * (__uint_as_float(vcur[4 * t + j] << 16) - Pt[t][j]);
-                // Delta0 = T00 bE0
-                const f16x8 Z8 = {0, 0, 0, 0, 0, 0, 0, 0};
-                f16x8 Bh = Z8, Bl = Z8;
+                for (int j = 0; j < 4; ++j)
+                    be[t][j] = op.beta[16 * t + 4 * grp + j] * (__uint_as_float(vcur[4 * t + j] << 16) - Pt[t][j]);
+            // Delta0 = T00 bE0 (two-term fp16 operand; slots of sub-block 1 are zero)
+            uint32_t bh[4] = {0u, 0u, 0u, 0u}, bl[4] = {0u, 0u, 0u, 0u};
+            split_f16x2(be[0][0], be[0][1], bh[0], bl[0]);
+            split_f16x2(be[0][2], be[0][3], bh[1], bl[1]);
+            f32x4 D0 = {0.f, 0.f, 0.f, 0.f};
+            {
+                const f16x8 th = lds_vec<f16x8>(&op.Tm[l16][8 * grp]);
+                D0 = mfma16(th, __builtin_bit_cast(f16x8, bh), D0);
+                D0 = mfma16(th, __builtin_bit_cast(f16x8, bl), D0);
+            }
+            uint32_t dh[4] = {0u, 0u, 0u, 0u}, dl[4] = {0u, 0u, 0u, 0u};
+            split_f16x2(D0[0], D0[1], dh[0], dl[0]);
+            split_f16x2(D0[2], D0[3], dh[1], dl[1]);
+            // Delta1 = T11 (bE1 - A10 Delta0)
+            f32x4 X = {0.f, 0.f, 0.f, 0.f};
+            {
+                const f16x8 ah = lds_vec<f16x8>(&op.A10[l16][8 * grp]);
+                X = mfma16(ah, __builtin_bit_cast(f16x8, dh), X);
+                X = mfma16(ah, __builtin_bit_cast(f16x8, dl), X);
+            }
+            bh[0] = bh[1] = bl[0] = bl[1] = 0u;
+            split_f16x2(be[1][0] - X[0], be[1][1] - X[1], bh[2], bl[2]);
+            split_f16x2(be[1][2] - X[2], be[1][3] - X[3], bh[3], bl[3]);
+            f32x4 D1 = {0.f, 0.f, 0.f, 0.f};
+            {
+                const f16x8 th = lds_vec<f16x8>(&op.Tm[16 + l16][8 * grp]);
+                D1 = mfma16(th, __builtin_bit_cast(f16x8, bh), D1);
+                D1 = mfma16(th, __builtin_bit_cast(f16x8, bl), D1);
+            }
+            split_f16x2(D1[0], D1[1], dh[2], dl[2]);
+            split_f16x2(D1[2], D1[3], dh[3], dl[3]);
+            const f16x8 DBh = __builtin_bit_cast(f16x8, dh), DBl = __builtin_bit_cast(f16x8, dl);
+            // O = (Q*gamma) S + M Delta (rows past the chunk's end are dropped)
+            const auto ro = chunk_rsrc(a.o, base + (long long)cs * ts, 4, nv, ts, D);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const half2s u = split16(be[0][j]);
-                    Bh[j] = u.hi;
-                    Bl[j] = u.lo;
-                }
-                f32x4 D0 = {0.f, 0.f, 0.f, 0.f};
-                {
-                    const f16x8 th = lds_vec<f16x8>(&op.Tm[l16][8 * grp]);
-                    D0 = mfma16(th, Bh, D0);
-                    D0 = mfma16(th, Bl, D0);
-                }
-                f16x8 DBh = Z8, DBl = Z8;
+            for (int t = 0; t < 2; ++t) {
+                const f16x8 mh = lds_vec<f16x8>(&op.M[0][16 * t + l16][8 * grp]);
+                const f16x8 ml = lds_vec<f16x8>(&op.M[1][16 * t + l16][8 * grp]);
+                f32x4 acc = Ot[t];
+                acc = mfma16(mh, DBh, acc);
+                acc = mfma16(mh, DBl, acc);
+                acc = mfma16(ml, DBh, acc);
+                const float ov[4] = {acc[0], acc[1], acc[2], acc[3]};
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const half2s u = split16(D0[j]);
-                    DBh[j] = u.hi;
-                    DBl[j] = u.lo;
-                }
-                // Delta1 = T11 (bE1 - A10 Delta0)
-                f32x4 X = {0.f, 0.f, 0.f, 0.f};
-                {
-                    const f16x8 ah = lds_vec<f16x8>(&op.A10[l16][8 * grp]);
-                    X = mfma16(ah, DBh, X);
-                    X = mfma16(ah, DBl, X);
-                }
-                Bh = Z8;
-                Bl = Z8;
+                for (int j = 0; j < 4; ++j)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ov[j]), ro, 2u * voff[4 * t + j], 0, 0);
+            }
+            // S <- Diag(gamma_last) S + Kt^T Delta (fp16 Kt, Delta's leading fp16 term)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const half2s u = split16(be[1][j] - X[j]);
-                    Bh[4 + j] = u.hi;
-                    Bl[4 + j] = u.lo;
-                }
-                f32x4 D1 = {0.f, 0.f, 0.f, 0.f};
-                {
-                    const f16x8 th = lds_vec<f16x8>(&op.Tm[16 + l16][8 * grp]);
-                    D1 = mfma16(th, Bh, D1);
-                    D1 = mfma16(th, Bl, D1);
-                }
+            for (int m = 0; m < 8; ++m) {
+                const float4 g4 = lds_vec<float4>(&op.gl[16 * m + 4 * grp]);
+                S[m][0] *= g4.x;
+                S[m][1] *= g4.y;
+                S[m][2] *= g4.z;
+                S[m][3] *= g4.w;
+                S[m] = mfma16(lds_vec<f16x8>(&op.KtT[16 * m + l16][8 * grp]), DBh, S[m]);
+            }
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const half2s u = split16(D1[j]);
-                    DBh[4 + j] = u.hi;
-                    DBl[4 + j] = u.lo;
-                }
-                // O = (Q*gamma) S + M Delta
-                float* och = a.o + base + (long long)cs * ts;
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const f16x8 mh = lds_vec<f16x8>(&op.M[0][16 * t + l16][8 * grp]);
-                    const f16x8 ml = lds_vec<f16x8>(&op.M[1][16 * t + l16][8 * grp]);
-                    f32x4 acc = Ot[t];
-                    acc = mfma16(mh, DBh, acc);
-                    acc = mfma16(mh, DBl, acc);
-                    acc = mfma16(ml, DBh, acc);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        if (16 * t + 4 * grp + j < nv) och[vofs + (uint32_t)(16 * t + j) * ts] = acc[j];
-                }
-                // S <- Diag(gamma_last) S + Kt^T Delta
-#pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    const float4 g4 = lds_vec<float4>(&op.gl[16 * m + 4 * grp]);
-                    S[m][0] *= g4.x;
-                    S[m][1] *= g4.y;
-                    S[m][2] *= g4.z;
-                    S[m][3] *= g4.w;
-                    const f16x8 kh = lds_vec<f16x8>(&op.KtT[0][16 * m + l16][8 * grp]);
-                    const f16x8 kl = lds_vec<f16x8>(&op.KtT[1][16 * m + l16][8 * grp]);
-                    S[m] = mfma16(kh, DBh, S[m]);
-                    S[m] = mfma16(kh, DBl, S[m]);
-                    S[m] = mfma16(kl, DBh, S[m]);
-                }
-#pragma unroll
-                for (int j = 0; j < 8; ++j) vcur[j] = vnxt[j];
+            for (int j = 0; j < 8; ++j) vcur[j] = vnxt[j];
             __syncthreads();
         }
         if (a.hT) {
@@ -501,25 +558,38 @@ __global__ __launch_bounds__(NT, 1) void kda_fwd_pipe(FwdArgs a) {
                     a.hT[sbase + (uint32_t)(16 * m + 4 * grp + j) * D + vc] = S[m][j];
         }
     } else {
+        // The helpers' chain sets the pace of the pipeline; the state waves
+        // have slack each chunk, so the helpers issue first on a shared SIMD.
+        __builtin_amdgcn_s_setprio(2);
+        const int hw = wave - NS;
+        const int cp = lane & 7, seg = lane >> 3;
+        const uint32_t coff = 16 * hw + 2 * cp;                        // channel pair offset
+        HOffs offs;
+#pragma unroll
+        for (int t = 0; t < SEG; ++t) {
+            offs.kq[t] = ((uint32_t)(SEG * seg + t) * ts + coff) * 2u;
+            offs.gg[t] = 2u * offs.kq[t];
+        }
+        offs.b = (uint32_t)(SEG * seg + (cp & 3)) * (uint32_t)a.H * 4u;
+        uint32_t ptarget = 0;
+        HFetch f;
+        auto prepare = [&](Ops& op, int cs) {
+            const bool more = cs + C < t1;
+            const int nnv = more ? min(C, t1 - cs - C) : 0;
+            factors(sm, op, f, hw, lane, more, a, base + (long long)(cs + C) * ts,
+                    bbase + (long long)(cs + C) * a.H, ts, offs, nnv);
+            __syncthreads();   // mid-chunk barrier
+            tiles(sm, op, hw, lane, ++ptarget);
+        };
         if (nch > 0) {
-            hfetch(f, a, base + (long long)t0 * ts, bbase + (long long)t0 * a.H, ts, hoff, min(C, t1 - t0), ht >> 6, ht);
-            const bool more = nch > 1;
-            prepare(sm, sm.op[0], f, min(C, t1 - t0), hw, lane, ht, htarget, more, a,
-                    base + (long long)(t0 + C) * ts, bbase + (long long)(t0 + C) * a.H, ts, hoff,
-                    more ? min(C, t1 - t0 - C) : 0);
+            hfetch(f, a, base + (long long)t0 * ts, bbase + (long long)t0 * a.H, ts, min(C, t1 - t0), offs);
+            prepare(sm.op[0], t0);
         }
         __syncthreads();
         for (int ci = 0; ci < nch; ++ci) {
-            const int cs = t0 + ci * C;
-            if (ci + 1 < nch) {
-                // registers of chunk ci+1 were fetched during the previous prepare()
-                const int ncs = cs + C;
-                const bool more = ci + 2 < nch;
-                const long long nb = base + (long long)(ncs + C) * ts, nbb = bbase + (long long)(ncs + C) * a.H;
-                const int nnv = more ? min(C, t1 - ncs - C) : 0;
-                prepare(sm, sm.op[(ci + 1) & 1], f, min(C, t1 - ncs), hw, lane, ht, htarget, more, a, nb, nbb, ts,
-                        hoff, nnv);
-            }
+            // registers of chunk ci+1 were fetched during the previous prepare()
+            if (ci + 1 < nch) prepare(sm.op[(ci + 1) & 1], t0 + (ci + 1) * C);
+            else __syncthreads();   // the mid-chunk barrier of the last chunk
             __syncthreads();
         }
     }
