@@ -536,7 +536,7 @@ __global__ __launch_bounds__(NT, 1) void kda_fwd_pipe(FwdArgs a) {
                 for (int j = 0; j < 4; ++j)
                     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ov[j]), ro, 2u * voff[4 * t + j], 0, 0);
             }
-            // S <- Diag(gamma_last) S + Kt^T Delta (fp16 Kt, Delta's leading fp16 term)
+            // S <- Diag(gamma_last) S + Kt^T Delta (single fp16 Kt, two-term Delta)
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
                 const float4 g4 = lds_vec<float4>(&op.gl[16 * m + 4 * grp]);
@@ -544,7 +544,9 @@ __global__ __launch_bounds__(NT, 1) void kda_fwd_pipe(FwdArgs a) {
                 S[m][1] *= g4.y;
                 S[m][2] *= g4.z;
                 S[m][3] *= g4.w;
-                S[m] = mfma16(lds_vec<f16x8>(&op.KtT[16 * m + l16][8 * grp]), DBh, S[m]);
+                const f16x8 kt = lds_vec<f16x8>(&op.KtT[16 * m + l16][8 * grp]);
+                S[m] = mfma16(kt, DBh, S[m]);
+                S[m] = mfma16(kt, DBl, S[m]);
             }
 #pragma unroll
             for (int j = 0; j < 8; ++j) vcur[j] = vnxt[j];
@@ -558,9 +560,6 @@ __global__ __launch_bounds__(NT, 1) void kda_fwd_pipe(FwdArgs a) {
                     a.hT[sbase + (uint32_t)(16 * m + 4 * grp + j) * D + vc] = S[m][j];
         }
     } else {
-        // The helpers' chain sets the pace of the pipeline; the state waves
-        // have slack each chunk, so the helpers issue first on a shared SIMD.
-        __builtin_amdgcn_s_setprio(2);
         const int hw = wave - NS;
         const int cp = lane & 7, seg = lane >> 3;
         const uint32_t coff = 16 * hw + 2 * cp;                        // channel pair offset
