@@ -68,6 +68,50 @@ def traffic_from_profile(workload: str):
     return float(m_b.group(1))
 
 
+def bench_decode(args):
+    """In-place decode steps: N sequences x 96 heads, one token each per step."""
+    import numpy as np
+    import torch
+    import workloads as W
+    import gated_delta_rule_63_amd as kda
+
+    N, H = args.decode, W.CONFIGS["c2"].H
+    cfg = W.variant("c2", B=N, T=1, H=H, h0=True, name=f"decode N={N}")
+    inp = W.make_inputs(cfg, args.seed)
+    dev = torch.device("cuda:0")
+    cvt = lambda x: torch.from_numpy(W.bf16_bits(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = cvt(inp.q), cvt(inp.k), cvt(inp.v)
+    g, beta = torch.from_numpy(inp.g).to(dev), torch.from_numpy(inp.beta).to(dev)
+    state = torch.from_numpy(inp.h0).to(dev)
+    o = torch.empty((N, 1, H, 128), dtype=torch.float32, device=dev)
+    step = lambda: kda.decode_step(q, k, v, g, beta, state=state, out=o, in_place=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    per_head = 3 * 256 + 512 + 4 + 512 + 2 * STATE_BYTES
+    bytes_ = N * H * per_head
+    achieved = bytes_ / (ms / 1e3) / 1e9
+    print(json.dumps({
+        "metric": f"KDA decode tokens/s (N={N} sequences, H={H}, D=128, bf16, state in place)",
+        "value": N / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"decode: {N} sequences x {H} heads, one token each, fp32 state read and written",
+                   "global_batch": N, "seq_len": 1, "heads": H, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "kda_decode_kernel",
+                     "alg_bytes_per_launch": bytes_},
+    }))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -81,6 +125,8 @@ def main():
     ap.add_argument("--path", choices=["fused", "staged"], default="fused",
                     help="fused: kda_fwd (the hot path); staged: kda_fwd_staged (five kernels)")
     ap.add_argument("--stages", action="store_true", help="also time each staged-path kernel on its own")
+    ap.add_argument("--decode", type=int, default=0, metavar="N",
+                    help="time the in-place decode step for N sequences (H = 96) instead of the prefill")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one device-to-device copy of this many MiB at the end (counter calibration)")
     args = ap.parse_args()
@@ -88,6 +134,10 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+
+    if args.decode:
+        bench_decode(args)
+        return
 
     import numpy as np
     import torch

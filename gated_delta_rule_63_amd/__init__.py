@@ -16,7 +16,7 @@ import torch
 
 from ._lib import KDA_BF16, KDA_F32, Desc, KDAError, Layout, lib, status_string  # noqa: F401
 
-__all__ = ["fwd", "fwd_staged", "Staged", "KDAError", "status_string", "version"]
+__all__ = ["fwd", "decode_step", "fwd_staged", "Staged", "KDAError", "status_string", "version"]
 
 D = 128
 
@@ -81,6 +81,36 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
     if rc != 0:
         raise KDAError(rc, "kda_fwd")
     return o, hT
+
+
+def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+                state: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                new_state: Optional[torch.Tensor] = None, in_place: bool = False,
+                stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """One decode step for N sequences: q, k, v, g [N, 1, H, 128]; beta [N, 1, H];
+    state [N, H, 128, 128] fp32 (None: zero). Returns (o fp32 [N, 1, H, 128], new state).
+    With in_place=True the new state overwrites `state`."""
+    _check_inputs(q, k, v, g, beta, None)
+    N, T, H, _ = q.shape
+    if T != 1:
+        raise ValueError("decode_step takes one token per sequence ([N, 1, H, 128])")
+    if state is not None and (state.dtype != torch.float32 or not state.is_contiguous()
+                              or tuple(state.shape) != (N, H, D, D)):
+        raise ValueError("state must be a contiguous float32 [N, H, 128, 128] tensor")
+    if in_place:
+        if state is None:
+            raise ValueError("in_place needs a state")
+        new_state = state
+    elif new_state is None:
+        new_state = torch.empty((N, H, D, D), dtype=torch.float32, device=q.device)
+    o = out if out is not None else torch.empty((N, 1, H, D), dtype=torch.float32, device=q.device)
+    d = _desc(q, None)
+    s = (stream or torch.cuda.current_stream(q.device)).cuda_stream
+    rc = lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o),
+                               _ptr(new_state), ctypes.byref(d), ctypes.c_void_p(s))
+    if rc != 0:
+        raise KDAError(rc, "kda_decode_step")
+    return o, new_state
 
 
 class Staged:

@@ -3,6 +3,7 @@
 #include "../../include/kda.h"
 
 #include <limits.h>
+#include <stdint.h>
 
 #include <algorithm>
 
@@ -46,6 +47,28 @@ kda_status_t check_desc(const kda_desc_t* d, bool varlen) {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+kda::FwdArgs fwd_args(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                      const int32_t* cu_seqlens, const float* h0, void* o, float* hT, const kda_desc_t* d) {
+    kda::FwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.cu = cu_seqlens;
+    a.h0 = h0;
+    a.o = static_cast<float*>(o);
+    a.hT = hT;
+    a.B = d->B;
+    a.T = d->T;
+    a.H = d->H;
+    a.N = d->num_seqs;
+    a.nchains = d->num_seqs * d->H;
+    return a;
+}
 
 // Layout of the staged path's workspace. Whether the descriptor is varlen is
 // not part of kda_desc_t, so the slot count covers both cases: the larger of
@@ -140,25 +163,28 @@ kda_status_t kda_fwd(const void* q, const void* k, const void* v, const float* g
                      float* hT, const kda_desc_t* desc, void* stream) {
     const kda_status_t st = check(q, k, v, g, beta, cu_seqlens, o, desc);
     if (st != KDA_OK) return st;
-    kda::FwdArgs a;
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.g = g;
-    a.beta = beta;
-    a.cu = cu_seqlens;
-    a.h0 = h0;
-    a.o = static_cast<float*>(o);
-    a.hT = hT;
-    a.B = desc->B;
-    a.T = desc->T;
-    a.H = desc->H;
-    a.N = desc->num_seqs;
-    a.nchains = desc->num_seqs * desc->H;
+    const kda::FwdArgs a = fwd_args(q, k, v, g, beta, cu_seqlens, h0, o, hT, desc);
     if (a.nchains == 0) return KDA_OK;
-    const hipError_t e = desc->in_dtype == KDA_F32
-                             ? kda::launch_fwd_serial(a, true, static_cast<hipStream_t>(stream))
-                             : kda::launch_fwd_pipe(a, static_cast<hipStream_t>(stream));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool f32 = desc->in_dtype == KDA_F32;
+    hipError_t e;
+    if (desc->T == 1 && !cu_seqlens && aligned16(o) && aligned16(h0) && aligned16(hT))
+        e = kda::launch_decode(a, f32, s);   // one token per sequence: a single recurrence step
+    else
+        e = f32 ? kda::launch_fwd_serial(a, true, s) : kda::launch_fwd_pipe(a, s);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status_t kda_decode_step(const void* q, const void* k, const void* v, const float* g,
+                             const float* beta, const float* state_in, void* o, float* state_out,
+                             const kda_desc_t* desc, void* stream) {
+    if (!desc) return KDA_ERR_NULL;
+    if (desc->T != 1 || desc->num_seqs != desc->B) return KDA_ERR_SHAPE;
+    const kda_status_t st = check(q, k, v, g, beta, nullptr, o, desc);
+    if (st != KDA_OK) return st;
+    if (!aligned16(o) || !aligned16(state_in) || !aligned16(state_out)) return KDA_ERR_UNSUPPORTED;
+    const kda::FwdArgs a = fwd_args(q, k, v, g, beta, nullptr, state_in, o, state_out, desc);
+    const hipError_t e = kda::launch_decode(a, desc->in_dtype == KDA_F32, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -27,5 +27,8 @@ hipError_t launch_fwd_serial(const FwdArgs& a, bool f32_inputs, hipStream_t stre
 // Helper waves prepare chunk i+1 while state waves advance chunk i (bf16 inputs).
 int pipe_workgroups(int nchains);
 hipError_t launch_fwd_pipe(const FwdArgs& a, hipStream_t stream);
+// One recurrence step per (sequence, head) (T = 1, no cu): the decode step.
+// o, h0 and hT must be 16-byte aligned.
+hipError_t launch_decode(const FwdArgs& a, bool f32_inputs, hipStream_t stream);
 
 }  // namespace kda

@@ -94,10 +94,38 @@ kda_status_t kda_fwd_check(const void* q, const void* k, const void* v, const fl
 /* The chunked KDA forward (prefill): o for every token and, when hT != NULL,
  * the final state of every (sequence, head). h0 == NULL starts from zero.
  * Runs as one fused kernel per (sequence, head, V-block) that reads every
- * input once; it needs no workspace. */
+ * input once; it needs no workspace. With T == 1 and no cu_seqlens (one
+ * token per batch row) and 16-byte aligned o, h0, hT, it runs the decode
+ * kernel of kda_decode_step instead. */
 kda_status_t kda_fwd(const void* q, const void* k, const void* v, const float* g,
                      const float* beta, const int32_t* cu_seqlens, const float* h0,
                      void* o, float* hT, const kda_desc_t* desc, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Decode step: one new token for each of N sequences, i.e. one step of the
+ * recurrence above per (sequence, head), applied to a state carried over from
+ * a prefill (the pages list decode as the next, not yet tuned, part of the
+ * interface: toolarium.ru page, section "Где ограничения прямо сейчас";
+ * donniechu.com page, section "Hạn chế & điều kiện").
+ *
+ *     S' = (I - beta k k^T) Diag(exp(g)) S + beta k v^T,    o = S'^T q
+ *
+ * desc: B = num_seqs = N, T = 1, H, K = V = 128, in_dtype bf16 or fp32,
+ * out_dtype fp32; desc->workspace is ignored.
+ *     q, k, v   [N, 1, H, 128]   in_dtype
+ *     g         [N, 1, H, 128]   fp32
+ *     beta      [N, 1, H]        fp32
+ *     state_in  [N, H, 128, 128] fp32 (NULL: zero state)
+ *     o         [N, 1, H, 128]   fp32
+ *     state_out [N, H, 128, 128] fp32 (NULL: not written)
+ * state_in == state_out (the same pointer) updates the state in place. o,
+ * state_in and state_out must be 16-byte aligned (KDA_ERR_UNSUPPORTED
+ * otherwise). Errors as for kda_fwd; T != 1 or num_seqs != B is
+ * KDA_ERR_SHAPE. One workgroup per (sequence, head); the state is read and
+ * written once (HBM-bound). */
+kda_status_t kda_decode_step(const void* q, const void* k, const void* v, const float* g,
+                             const float* beta, const float* state_in, void* o, float* state_out,
+                             const kda_desc_t* desc, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Staged path. The same chunked forward as four kernels (plus a chunk map)

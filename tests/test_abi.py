@@ -76,6 +76,22 @@ def test_fwd_rejects_before_launch(K):
     assert K.lib().kda_stage_output(P, ctypes.byref(d), None) == -5                       # too small
 
 
+def test_decode_rejects_before_launch(K):
+    """kda_decode_step: shape, null and alignment errors return before any launch."""
+    L = K.lib()
+    A = ctypes.c_void_p(0x10000)                    # 16-byte aligned stand-in pointer
+    M = ctypes.c_void_p(0x10004)                    # misaligned
+    d = desc(K, B=4, T=2, N=4)
+    assert L.kda_decode_step(A, A, A, A, A, None, A, None, ctypes.byref(d), None) == -2   # T != 1
+    d = desc(K, B=4, T=1, N=3)
+    assert L.kda_decode_step(A, A, A, A, A, None, A, None, ctypes.byref(d), None) == -2   # N != B
+    d = desc(K, B=4, T=1, N=4)
+    assert L.kda_decode_step(None, A, A, A, A, None, A, None, ctypes.byref(d), None) == -1
+    assert L.kda_decode_step(A, A, A, A, A, M, A, None, ctypes.byref(d), None) == -3      # misaligned state
+    assert L.kda_decode_step(A, A, A, A, A, None, M, None, ctypes.byref(d), None) == -3   # misaligned o
+    assert L.kda_decode_step(A, A, A, A, A, None, A, None, None, None) == -1
+
+
 def test_staged_layout(K):
     L = K.Layout()
     d = desc(K, B=1, T=8192, H=96)
