@@ -46,9 +46,11 @@ def alg_bytes(cfg) -> int:
 
 
 def kernel_source_hash() -> str:
+    """Hash of the sources the fused kernel is compiled from (its file and the
+    device helpers it includes), so a counter summary is tied to that kernel."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gated_delta_rule_63_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in ("kda_fused_pipe.hip", "kda_device.h"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

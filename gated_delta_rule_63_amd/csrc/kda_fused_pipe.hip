@@ -449,8 +449,14 @@ __global__ __launch_bounds__(NT, 1) void kda_fwd_pipe(FwdArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 S[m][j] = a.h0 ? a.h0[sbase + (uint32_t)(16 * m + 4 * grp + j) * D + vc] : 0.f;
+        // Complete the h0 loads here (s_waitcnt vmcnt(0)): otherwise the
+        // compiler cannot prove them done inside the chunk loop and waits there
+        // for every outstanding load, including the next chunk's prefetch.
+        __builtin_amdgcn_s_waitcnt(0x0F70);
         if (nch > 0) {
-            vfetch(vcur, 0);
+            vfetch(vnxt, 0);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) vcur[j] = vnxt[j];
             __syncthreads();   // the helpers' mid-chunk barrier of chunk 0
         }
         __syncthreads();
@@ -458,6 +464,9 @@ __global__ __launch_bounds__(NT, 1) void kda_fwd_pipe(FwdArgs a) {
             const int cs = t0 + ci * C;
             const int nv = min(C, t1 - cs);
             const Ops& op = sm.op[ci & 1];
+            // V of the next chunk, copied into vcur at the end of this one: the
+            // loaded registers never stay pending across the loop edge, so the
+            // waits for them are exact and fall after this chunk's work.
             if (ci + 1 < nch) vfetch(vnxt, ci + 1);
             // the state as a B operand: rows in kperm order, rounded to fp16
             f16x8 SBh[4];

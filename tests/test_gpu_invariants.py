@@ -64,6 +64,14 @@ def test_varlen_equals_per_sequence_runs():
         sub["cu"] = None
         sub["h0"] = t["h0"][n:n + 1].contiguous()
         on, hn = fwd(sub)
+        if b - a == 1:
+            # a one-token call without cu_seqlens runs the fp32 decode kernel,
+            # not the chunked kernel with its fp16/bf16 operands: the two agree
+            # to the parity bars, not bitwise
+            tol_o, tol_s = TOL["bf16"]
+            assert rel_err(o[:, a:b].cpu().numpy(), on.cpu().numpy()) <= tol_o, f"sequence {n}"
+            assert rel_err(h[n].cpu().numpy(), hn[0].cpu().numpy()) <= tol_s, f"sequence {n} state"
+            continue
         assert bool((on == o[:, a:b]).all()), f"sequence {n}"
         assert bool((hn[0] == h[n]).all()), f"sequence {n} state"
 
