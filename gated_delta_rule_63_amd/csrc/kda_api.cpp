@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "kda_launch.h"
 #include "kda_stages.h"
@@ -131,6 +132,23 @@ kda_status_t stage_args(const kda_desc_t* d, const int32_t* cu, kda::StageArgs* 
 
 kda_status_t hip_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
 
+// Compute units of the current device, read once per device (the attribute
+// cannot change while the process runs; concurrent first calls store the
+// same value).
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 }  // namespace
 
 extern "C" {
@@ -171,7 +189,7 @@ kda_status_t kda_fwd(const void* q, const void* k, const void* v, const float* g
     if (desc->T == 1 && !cu_seqlens && aligned16(o) && aligned16(h0) && aligned16(hT))
         e = kda::launch_decode(a, f32, s);   // one token per sequence: a single recurrence step
     else
-        e = f32 ? kda::launch_fwd_serial(a, true, s) : kda::launch_fwd_pipe(a, s);
+        e = f32 ? kda::launch_fwd_serial(a, true, s) : kda::launch_fwd_pipe(a, device_cus(), s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

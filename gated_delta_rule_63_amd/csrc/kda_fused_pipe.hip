@@ -33,11 +33,17 @@ namespace kda {
 namespace pipe {
 
 constexpr int C = 32;          // chunk length (two 16-token sub-blocks)
-constexpr int NS = 4;          // state waves, 16 V columns each
 constexpr int NH = 8;          // helper waves, 16 channels each
-constexpr int NT = 64 * (NS + NH);
-constexpr int VB = 16 * NS;    // V columns per workgroup
-constexpr int P = D / VB;      // workgroups per (sequence, head)
+// NS state waves (16 V columns each) per workgroup: 4, 2 or 1, so a (sequence,
+// head) is split over P = 2, 4 or 8 workgroups. Every split computes the same
+// values in the same order per column; a finer split only repeats the helper
+// work, which pays when there are too few chains to fill the chip.
+template <int NS>
+struct Split {
+    static constexpr int NT = 64 * (NS + NH);   // threads per workgroup
+    static constexpr int VB = 16 * NS;          // V columns per workgroup
+    static constexpr int P = D / VB;            // workgroups per (sequence, head)
+};
 constexpr int SEG = 4;         // tokens per helper lane
 constexpr int NSEG = C / SEG;  // segments per chunk (lanes 8*seg + cp)
 constexpr int LDP = D + 8;     // row pitch of a 2-byte [token][channel] array
@@ -386,7 +392,9 @@ __device__ __forceinline__ void tiles(Smem& sm, Ops& op, int hw, int lane, uint3
     }
 }
 
-__global__ __launch_bounds__(NT, 1) void kda_fwd_pipe(FwdArgs a) {
+template <int NS>
+__global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
+    constexpr int NT = Split<NS>::NT, VB = Split<NS>::VB, P = Split<NS>::P;
     __shared__ Smem sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, grp = lane >> 4;
@@ -604,15 +612,27 @@ __global__ __launch_bounds__(NT, 1) void kda_fwd_pipe(FwdArgs a) {
 }
 }  // namespace pipe
 
-int pipe_workgroups(int nchains) {
-    const int groups = (nchains + 7) / 8;
-    return groups * 8 * pipe::P;
+int pipe_state_waves(int nchains, int cus) {
+    if ((long long)nchains * 8 <= cus) return 1;
+    if ((long long)nchains * 4 <= cus) return 2;
+    return 4;
 }
 
-hipError_t launch_fwd_pipe(const FwdArgs& a, hipStream_t stream) {
-    const int grid = pipe_workgroups(a.nchains);
+int pipe_workgroups(int nchains, int state_waves) {
+    const int groups = (nchains + 7) / 8;
+    return groups * 8 * (D / (16 * state_waves));
+}
+
+hipError_t launch_fwd_pipe(const FwdArgs& a, int cus, hipStream_t stream) {
+    const int ns = pipe_state_waves(a.nchains, cus);
+    const int grid = pipe_workgroups(a.nchains, ns);
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL(pipe::kda_fwd_pipe, dim3(grid), dim3(pipe::NT), 0, stream, a);
+    if (ns == 1)
+        hipLaunchKernelGGL(pipe::kda_fwd_pipe<1>, dim3(grid), dim3(pipe::Split<1>::NT), 0, stream, a);
+    else if (ns == 2)
+        hipLaunchKernelGGL(pipe::kda_fwd_pipe<2>, dim3(grid), dim3(pipe::Split<2>::NT), 0, stream, a);
+    else
+        hipLaunchKernelGGL(pipe::kda_fwd_pipe<4>, dim3(grid), dim3(pipe::Split<4>::NT), 0, stream, a);
     return hipGetLastError();
 }
 

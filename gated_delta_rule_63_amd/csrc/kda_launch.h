@@ -25,8 +25,11 @@ struct FwdArgs {
 int serial_workgroups(int nchains);
 hipError_t launch_fwd_serial(const FwdArgs& a, bool f32_inputs, hipStream_t stream);
 // Helper waves prepare chunk i+1 while state waves advance chunk i (bf16 inputs).
-int pipe_workgroups(int nchains);
-hipError_t launch_fwd_pipe(const FwdArgs& a, hipStream_t stream);
+// The chain is split over 128 / (16 * state_waves) workgroups; state_waves is
+// 4, 2 or 1, the largest that still fills `cus` compute units.
+int pipe_state_waves(int nchains, int cus);
+int pipe_workgroups(int nchains, int state_waves);
+hipError_t launch_fwd_pipe(const FwdArgs& a, int cus, hipStream_t stream);
 // One recurrence step per (sequence, head) (T = 1, no cu): the decode step.
 // o, h0 and hT must be 16-byte aligned.
 hipError_t launch_decode(const FwdArgs& a, bool f32_inputs, hipStream_t stream);

@@ -136,3 +136,21 @@ def test_c4_handoff_and_oracle():
     es = rel_err(h.cpu().numpy()[:, heads], rs)
     log(f"[inv] c4 heads {heads}: err_o {eo:.2e} err_hT {es:.2e}")
     assert eo <= TOL["bf16"][0] and es <= TOL["bf16"][1]
+
+
+def test_split_over_workgroups_is_bitwise():
+    """The number of workgroups a head is split over (2, 4 or 8, chosen from the
+    number of chains) does not change any value: heads 0-19 of an 80-head run
+    (two-way split) equal the same heads run as a 20-head (eight-way) and a
+    40-head (four-way) problem."""
+    import torch
+    cfg = W.variant("c2", T=300, H=80, h0=True, gate="mild", name="split-ways")
+    t = to_device(W.make_inputs(cfg, 8), "bf16")
+    o80, h80 = fwd(t)
+    for H in (20, 40):
+        sub = {k: (v[:, :, :H].contiguous() if k in ("q", "k", "v", "g", "beta") else v) for k, v in t.items()}
+        sub["h0"] = t["h0"][:, :H].contiguous()
+        o, h = fwd(sub)
+        log(f"[split] H={H}: max|o - o80| = {float((o - o80[:, :, :H]).abs().max()):.3g}")
+        assert bool((o == o80[:, :, :H]).all()), f"H={H} output"
+        assert bool((h == h80[:, :H]).all()), f"H={H} state"
