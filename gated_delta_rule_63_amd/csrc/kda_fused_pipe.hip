@@ -4,24 +4,26 @@
 // Same chunk algebra as the serial kernel (kda_fused_serial.hip), organised as
 // a two-stage pipeline inside each workgroup:
 //   * NS "state" waves each own 16 V columns of the 128 x 128 fp32 state of one
-//     (sequence, head) and run only the sequential, MFMA-bound part for chunk i:
+//     (sequence, head) and run the sequential part of chunk i:
 //        P = (K*gamma) S,  Delta = (I + A)^{-1} Diag(beta) (V - P),
 //        O = (Q*gamma) S + M Delta,  S <- Diag(gamma_last) S + Kt^T Delta;
+//     before the mid-chunk barrier they also invert the two diagonal blocks
+//     of I + A of chunk i (fp32 MFMA), from A that the helpers left in LDS.
 //   * NH "helper" waves prepare chunk i+1 at the same time. A helper lane owns
 //     two channels of four consecutive tokens; one wave holds all eight
 //     segments of its channels, so the in-chunk log-gate scan needs no
-//     workgroup synchronisation. The lane forms every gated factor of its
-//     eight elements; after the mid-chunk barrier the helpers build the
-//     gated K K^T blocks (A, bf16 MFMA), the gated Q K^T blocks (M, fp32
-//     MFMA) and the inverses of the diagonal blocks of I + A (fp32 MFMA),
-//     writing the state waves' operands into the other half of a
-//     double-buffered LDS area.
-// Two workgroup barriers per chunk: one in the middle, where the helpers have
-// finished the factors of chunk i+1 and the state waves the products with the
-// old state of chunk i, and one at the end, which hands the operand buffers
-// over. Two helper waves share each SIMD with one state wave: a single wave
-// issues a VALU instruction at most every other slot, so the helpers' element
-// work needs two waves per SIMD.
+//     workgroup synchronisation. Before the mid-chunk barrier the lanes form
+//     every gated factor of their eight elements (VALU work); after it the
+//     helpers build the gated K K^T blocks (A) and the gated Q K^T blocks (M)
+//     on bf16 MFMA, writing the state waves' operands into the other half of
+//     a double-buffered LDS area.
+// So the element work of chunk i+1 overlaps the inversion and the products
+// with the old state of chunk i, and the block products of chunk i+1 overlap
+// the solve and state update of chunk i. Two workgroup barriers per chunk: the
+// mid-chunk one, and one at the end, which hands the operand buffers over.
+// Two helper waves share each SIMD with one state wave: a single wave issues a
+// VALU instruction at most every other slot, so the helpers' element work
+// needs two waves per SIMD.
 // The split into a chunk-parallel preparation and a sequential recurrence is
 // the pages' two-kernel design (toolarium.ru page, section "Где ограничения
 // прямо сейчас"); here the two run concurrently on one CU so that each input
@@ -97,31 +99,30 @@ struct alignas(16) Ops {
     _Float16 Tm[C][TP];             // block-diagonal (I + A)^{-1}, [row][kperm(col)]
     _Float16 A10[16][TP];           // A rows 16-31, cols 0-15, [row][kperm(col)]
     _Float16 M[2][C][TP];           // lower gated Q K^T, [hi, lo][row][kperm(col)]
+    float Af[2][16][16];            // diagonal blocks A00, A11 in fp32, [row][col]
     float gl[D];                    // exp(Gamma_last), the chunk's decay per channel
     float beta[C];
 };
 
+// Gated factors of one chunk, referenced to Gamma at the chunk's token 15
+// (Gamma_ref): the key and query factors of A and M. Rows at srow().
 struct alignas(16) Smem {
     Ops op[2];
-    __bf16 Ka[ROWS32];              // k * exp(Gamma_r - Gamma_mid(block)), rows at srow()
-    __bf16 Kb[ROWS32];              // k * exp(Gamma_mid(block) - Gamma_r)
-    __bf16 Kr[ROWS16];              // block-0 keys referenced to block 1's middle
-    float Qa[C][LD32];              // q * exp(Gamma_r - Gamma_mid(block)), fp32 for M
-    float Kb32[C][LD32];            // Kb in fp32 for M
-    float Kr32[16][LD32];           // Kr in fp32 for M
+    __bf16 Ka[ROWS32];              // k * exp(Gamma_r - Gamma_ref), rounded to nearest
+    __bf16 Kbh[ROWS32];             // k * exp(Gamma_ref - Gamma_r) = Kbh + Kbl
+    __bf16 Kbl[ROWS32];
+    __bf16 Qah[ROWS32];             // q * exp(Gamma_r - Gamma_ref) = Qah + Qal
+    __bf16 Qal[ROWS32];
     float2 segsum[NH][8][NSEG];     // per helper wave: segment sums of each channel pair
-    f32x4 mpart[64];                // half of the M11 block, handed from one helper wave to another
-    uint32_t pcount;                // hand-over counter of mpart
 };
 
-// Waits until an LDS counter reaches target. The wait is bounded; under
-// correct use it never runs out.
-__device__ __forceinline__ void wait_count(const uint32_t* cnt, uint32_t target) {
-    for (uint32_t spin = 0; spin < (1u << 20); ++spin) {
-        if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
-        __builtin_amdgcn_s_sleep(1);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+// x = hi + lo for a pair of floats: hi is x cut to bf16 (its upper 16 bits, so
+// x - hi is exact), lo is that remainder rounded to bf16; together they carry
+// about 16 significant bits.
+__device__ __forceinline__ void split_bf16x2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+    const uint32_t u0 = __float_as_uint(x0), u1 = __float_as_uint(x1);
+    hi = __builtin_amdgcn_perm(u1, u0, 0x07060302u);   // upper halves: x0 low word, x1 high word
+    lo = pack_bf16(x0 - __uint_as_float(u0 & 0xffff0000u), x1 - __uint_as_float(u1 & 0xffff0000u));
 }
 
 __device__ __forceinline__ float2 bf2(uint32_t u) {
@@ -161,15 +162,16 @@ __device__ __forceinline__ void hfetch(HFetch& f, const FwdArgs& a, long long cb
 // then the fetch of the chunk after it into the same registers.
 //
 // In-chunk cumulative log-gate Gamma, per channel, from the eight segment sums
-// S0..S7 (segments 0-3 form sub-block 0, segments 4-7 sub-block 1). Factors
-// are referenced to the middle of their sub-block (Gamma at its token 7):
-// S0+S1 for sub-block 0 and tau0+S4+S5 for sub-block 1 (tau0 = S0+..+S3), so
-// each stays within exp(+-40) for g >= -5.
-__device__ __forceinline__ void factors(Smem& sm, Ops& op, HFetch& f, int hw, int lane,
+// S0..S7 of 4-token segments. Every factor of A and M is referenced to
+// Gamma_ref = Gamma at token 15 = S0+..+S3, so exponents stay within
+// [-80, 75] for g in [-5, 0]: k*exp(Gamma_r - Gamma_ref) and
+// k*exp(Gamma_ref - Gamma_i) multiply to k k exp(Gamma_r - Gamma_i) for every
+// pair of tokens in the chunk. wpre holds this lane's weights of S0..S6 in
+// Gamma at its segment start minus Gamma_ref (-1, 0 or +1).
+__device__ __forceinline__ void factors(Smem& sm, Ops& op, HFetch& f, int hw, int lane, const float (&wpre)[NSEG - 1],
                                         bool fetch_next, const FwdArgs& a, long long nbase, long long nbeta,
                                         uint32_t ts, const HOffs& offs, int nnv) {
     const int cp = lane & 7, seg = lane >> 3;
-    const int b = seg >> 2;
     const int c0 = 16 * hw + 2 * cp;
 
     float L[2][SEG], kv[2][SEG], qv[2][SEG];
@@ -199,25 +201,20 @@ __device__ __forceinline__ void factors(Smem& sm, Ops& op, HFetch& f, int hw, in
         const float4 v = lds_vec<float4>(&sm.segsum[hw][cp][s]);
         St[0][s] = v.x; St[1][s] = v.y; St[0][s + 1] = v.z; St[1][s + 1] = v.w;
     }
-    float d[2][SEG], c1[2], c2[2], c3[2];
+    float d[2][SEG], c1[2], c2[2];
 #pragma unroll
     for (int ch = 0; ch < 2; ++ch) {
         const float* S = St[ch];
-        const float tau0 = S[0] + S[1] + S[2] + S[3];
-        const float tau1 = S[4] + S[5] + S[6] + S[7];
-        const float rho0 = S[0] + S[1], rho1 = S[4] + S[5];   // block-local middles
-        // sum of the earlier segments of this lane's sub-block
-        float pre = 0.f;
+        const float ref = (S[0] + S[1]) + (S[2] + S[3]);
+        const float last = (S[4] + S[5]) + (S[6] + S[7]);      // Gamma_last - Gamma_ref
+        float moff = 0.f;
 #pragma unroll
-        for (int s = 0; s < NSEG - 1; ++s)
-            if (s < seg && (s >> 2) == b) pre += S[s];
-        const float rho = b ? rho1 : rho0;
-        c1[ch] = ex2((b ? tau0 + rho1 : rho0) * LOG2E);                 // exp(Gamma_mid)              -> K*gamma, Q*gamma
-        c2[ch] = ex2((b ? tau1 - rho1 : tau0 + tau1 - rho0) * LOG2E);   // exp(Gamma_last - Gamma_mid) -> Kt
-        c3[ch] = ex2((tau0 + rho1 - rho0) * LOG2E);                     // block 0 -> block 1's middle -> Kr
-        const float moff = (pre - rho) * LOG2E;
+        for (int s = 0; s < NSEG - 1; ++s) moff = fmaf(wpre[s], S[s], moff);
+        c1[ch] = ex2(ref * LOG2E);     // exp(Gamma_ref)              -> K*gamma, Q*gamma
+        c2[ch] = ex2(last * LOG2E);    // exp(Gamma_last - Gamma_ref) -> Kt
+        const float m2 = moff * LOG2E;
 #pragma unroll
-        for (int t = 0; t < SEG; ++t) d[ch][t] = fmaf(L[ch][t], LOG2E, moff);
+        for (int t = 0; t < SEG; ++t) d[ch][t] = fmaf(L[ch][t], LOG2E, m2);
     }
     if (seg == 0) *reinterpret_cast<float2*>(&op.gl[c0]) = make_float2(c1[0] * c2[0], c1[1] * c2[1]);
 
@@ -226,8 +223,8 @@ __device__ __forceinline__ void factors(Smem& sm, Ops& op, HFetch& f, int hw, in
 #pragma unroll
     for (int t = 0; t < SEG; ++t) {
         const int r = SEG * seg + t;
-        const int so = srow(r);
-        float ka[2], qa[2], kb[2], kr[2];
+        const int so = srow(r) + c0;
+        float ka[2], qa[2], kb[2];
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
             const float e1 = ex2(d[ch][t]), e2 = ex2(-d[ch][t]);
@@ -235,18 +232,17 @@ __device__ __forceinline__ void factors(Smem& sm, Ops& op, HFetch& f, int hw, in
             qa[ch] = qv[ch][t] * e1;
             kb[ch] = kv[ch][t] * e2;
             kt[ch][t] = kb[ch] * c2[ch];
-            kr[ch] = kb[ch] * c3[ch];
         }
-        *reinterpret_cast<uint32_t*>(&sm.Ka[so + c0]) = pack_bf16(ka[0], ka[1]);
-        *reinterpret_cast<uint32_t*>(&sm.Kb[so + c0]) = pack_bf16(kb[0], kb[1]);
-        *reinterpret_cast<float2*>(&sm.Qa[r][c0]) = make_float2(qa[0], qa[1]);
-        *reinterpret_cast<float2*>(&sm.Kb32[r][c0]) = make_float2(kb[0], kb[1]);
-        if (b == 0) {
-            *reinterpret_cast<uint32_t*>(&sm.Kr[so + c0]) = pack_bf16(kr[0], kr[1]);
-            *reinterpret_cast<float2*>(&sm.Kr32[r][c0]) = make_float2(kr[0], kr[1]);
-        }
-        *reinterpret_cast<uint32_t*>(&op.Kg[so + cpos]) = pack_f16(ka[0] * c1[0], ka[1] * c1[1]);
-        *reinterpret_cast<uint32_t*>(&op.Qg[so + cpos]) = pack_f16(qa[0] * c1[0], qa[1] * c1[1]);
+        uint32_t kbh, kbl, qah, qal;
+        split_bf16x2(kb[0], kb[1], kbh, kbl);
+        split_bf16x2(qa[0], qa[1], qah, qal);
+        *reinterpret_cast<uint32_t*>(&sm.Ka[so]) = pack_bf16(ka[0], ka[1]);
+        *reinterpret_cast<uint32_t*>(&sm.Kbh[so]) = kbh;
+        *reinterpret_cast<uint32_t*>(&sm.Kbl[so]) = kbl;
+        *reinterpret_cast<uint32_t*>(&sm.Qah[so]) = qah;
+        *reinterpret_cast<uint32_t*>(&sm.Qal[so]) = qal;
+        *reinterpret_cast<uint32_t*>(&op.Kg[srow(r) + cpos]) = pack_f16(ka[0] * c1[0], ka[1] * c1[1]);
+        *reinterpret_cast<uint32_t*>(&op.Qg[srow(r) + cpos]) = pack_f16(qa[0] * c1[0], qa[1] * c1[1]);
     }
     // K~^T: the lane's four tokens are four consecutive kperm positions
     const int tp = kperm(SEG * seg);
@@ -254,25 +250,6 @@ __device__ __forceinline__ void factors(Smem& sm, Ops& op, HFetch& f, int hw, in
     for (int ch = 0; ch < 2; ++ch)
         *reinterpret_cast<uint2*>(&op.KtT[c0 + ch][tp]) =
             make_uint2(pack_f16(kt[ch][0], kt[ch][1]), pack_f16(kt[ch][2], kt[ch][3]));
-}
-
-// 16 x 16 block of M on fp32 MFMA: rows from Qa (tokens qr..qr+15), columns
-// from B32 (tokens 0..15 of that array). K-slot g of the four products taken
-// from one 16-byte read is channel 16*mq + 4*g + (0..3); channels 16*MQ0 up
-// to 16*MQ1 are summed.
-template <int MQ0 = 0, int MQ1 = D / 16>
-__device__ __forceinline__ f32x4 mtile(const float (*Qa)[LD32], const float (*B32)[LD32], int qr, int l16, int grp) {
-    f32x4 m0 = {0.f, 0.f, 0.f, 0.f}, m1 = m0;
-#pragma unroll
-    for (int mq = MQ0; mq < MQ1; ++mq) {
-        const float4 qa = lds_vec<float4>(&Qa[qr + l16][16 * mq + 4 * grp]);
-        const float4 kb = lds_vec<float4>(&B32[l16][16 * mq + 4 * grp]);
-        m0 = mfma16x4(qa.x, kb.x, m0);
-        m1 = mfma16x4(qa.y, kb.y, m1);
-        m0 = mfma16x4(qa.z, kb.z, m0);
-        m1 = mfma16x4(qa.w, kb.w, m1);
-    }
-    return m0 + m1;
 }
 
 // X Y for 16 x 16 fp32 matrices on fp32 MFMA, from X^T and Y in accumulator
@@ -322,74 +299,78 @@ __device__ __forceinline__ void store_tile(_Float16 (*hi)[TP], _Float16 (*lo)[TP
     }
 }
 
-// Helpers, step 2: A and M blocks, and the inverses of the diagonal blocks.
-//   hw 0: A00 -> T00   hw 1: A11 -> T11   hw 2: M00   hw 3: M10   hw 4: A10
-//   hw 6, 7: M11, half of the channels each
-// An M block is 32 fp32 MFMAs, as is the inverse of a diagonal block of I + A;
-// helper wave hw shares SIMD hw % 4 with the other helper and one state wave,
-// so this spreads the fp32 products evenly over the four matrix cores.
-// The zero blocks of Tm, A10 and M are written once, at the kernel's start.
-__device__ __forceinline__ void tiles(Smem& sm, Ops& op, int hw, int lane, uint32_t ptarget) {
+// Helpers, step 2: the gated K K^T blocks of A (two-term keys) and the gated
+// Q K^T blocks of M (three terms), bf16 MFMA with fp32 accumulation:
+//   hw 0: A00   hw 1: A11   hw 2: A10   hw 3: M00   hw 4: M10   hw 5: M11
+// A00 and A11 go to the state waves in fp32 (they invert I + A there); A10 and
+// M as fp16 operands. The zero blocks of Tm, A10 and M are written once, at
+// the kernel's start.
+__device__ __forceinline__ void tiles(Smem& sm, Ops& op, int hw, int lane) {
     const int l16 = lane & 15, grp = lane >> 4;
-    if (hw <= 1) {
-        // A_bb and its transpose (the same products with the operands swapped)
-        const int rb = hw;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acct = acc;
+    if (hw <= 2) {
+        // A[r][i] = beta_r (Ka_r . Kb_i): lane holds column i = l16 of rows r = 4grp + j
+        const int rb = hw == 0 ? 0 : 16, cb = hw == 1 ? 16 : 0;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = acc;
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
-            const int off = srow(16 * rb + l16) + 32 * kk + 8 * grp;
-            const bf16x8 ka = lds_vec<bf16x8>(&sm.Ka[off]), kb = lds_vec<bf16x8>(&sm.Kb[off]);
-            acc = mfma16(ka, kb, acc);
-            acct = mfma16(kb, ka, acct);
+            const int ko = 32 * kk + 8 * grp;
+            const bf16x8 ka = lds_vec<bf16x8>(&sm.Ka[srow(rb + l16) + ko]);
+            acc = mfma16(ka, lds_vec<bf16x8>(&sm.Kbh[srow(cb + l16) + ko]), acc);
+            acc2 = mfma16(ka, lds_vec<bf16x8>(&sm.Kbl[srow(cb + l16) + ko]), acc2);
         }
-        // A[r][i] = beta_r (Ka_r . Kb_i) for i < r: lane holds column i = l16 of rows r = 4grp + j,
-        // and A^T: column r = l16 of rows i = 4grp + j.
-        const float bcol = op.beta[16 * rb + l16];
-        f32x4 A, At, ImA;
+        acc += acc2;
+        if (hw < 2) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 4 * grp + j;
-            A[j] = (l16 < r) ? op.beta[16 * rb + r] * acc[j] : 0.f;
-            At[j] = (l16 > r) ? bcol * acct[j] : 0.f;
-            ImA[j] = (l16 == r ? 1.f : 0.f) - A[j];
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * grp + j;
+                op.Af[hw][r][l16] = (l16 < r) ? op.beta[rb + r] * acc[j] : 0.f;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] *= op.beta[16 + 4 * grp + j];
+            store_tile<false>(op.A10, nullptr, acc, 0, 0, false, l16, grp);
         }
-        // (I + A)^{-1} = (I - A)(I + A^2)(I + A^4)(I + A^8): A is strictly
-        // lower triangular, so A^16 = 0 and the product is the whole Neumann
-        // series (the factors commute).
-        const f32x4 Z = {0.f, 0.f, 0.f, 0.f};
-        const f32x4 A2 = mprod(At, A, Z), A2t = mprod(A, At, Z);
-        const f32x4 Q1 = mprod(A2t, ImA, ImA);               // (I + A^2)(I - A)
-        const f32x4 A4 = mprod(A2t, A2, Z), A4t = mprod(A2, A2t, Z);
-        const f32x4 Q2 = mprod(A4t, Q1, Q1);                 // (I + A^4) Q1
-        const f32x4 A8t = mprod(A4, A4t, Z);
-        const f32x4 Tb = mprod(A8t, Q2, Q2);                 // (I + A^8) Q2
-        store_tile<false>(op.Tm, nullptr, Tb, 16 * rb, 16 * rb, false, l16, grp);
-    } else if (hw == 4) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    } else if (hw <= 5) {
+        // M[r][i] = Qa_r . Kb_i (i <= r) = Qah Kbh + Qah Kbl + Qal Kbh
+        const int rb = hw == 3 ? 0 : 16, cb = hw == 5 ? 16 : 0;
+        f32x4 m0 = {0.f, 0.f, 0.f, 0.f}, m1 = m0, m2 = m0;
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
-            const int off = 32 * kk + 8 * grp;
-            acc = mfma16(lds_vec<bf16x8>(&sm.Ka[srow(16 + l16) + off]), lds_vec<bf16x8>(&sm.Kr[srow(l16) + off]), acc);
+            const int ko = 32 * kk + 8 * grp;
+            const bf16x8 qh = lds_vec<bf16x8>(&sm.Qah[srow(rb + l16) + ko]);
+            const bf16x8 ql = lds_vec<bf16x8>(&sm.Qal[srow(rb + l16) + ko]);
+            const bf16x8 kh = lds_vec<bf16x8>(&sm.Kbh[srow(cb + l16) + ko]);
+            const bf16x8 kl = lds_vec<bf16x8>(&sm.Kbl[srow(cb + l16) + ko]);
+            m0 = mfma16(qh, kh, m0);
+            m1 = mfma16(qh, kl, m1);
+            m2 = mfma16(ql, kh, m2);
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] *= op.beta[16 + 4 * grp + j];
-        store_tile<false>(op.A10, nullptr, acc, 0, 0, false, l16, grp);
-    } else if (hw == 2) {
-        store_tile<true>(op.M[0], op.M[1], mtile(sm.Qa, sm.Kb32, 0, l16, grp), 0, 0, true, l16, grp);
-    } else if (hw == 3) {
-        store_tile<true>(op.M[0], op.M[1], mtile(sm.Qa, sm.Kr32, 16, l16, grp), 16, 0, false, l16, grp);
-    } else if (hw == 6) {
-        // channels 0-63 of M11, handed to hw 7
-        sm.mpart[lane] = mtile<0, D / 32>(&sm.Qa[16], &sm.Kb32[16], 0, l16, grp);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        if (lane == 0) __hip_atomic_fetch_add(&sm.pcount, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    } else if (hw == 7) {
-        // channels 64-127 of M11, plus hw 6's half
-        f32x4 m = mtile<D / 32, D / 16>(&sm.Qa[16], &sm.Kb32[16], 0, l16, grp);
-        wait_count(&sm.pcount, ptarget);
-        m += sm.mpart[lane];
-        store_tile<true>(op.M[0], op.M[1], m, 16, 16, true, l16, grp);
+        store_tile<true>(op.M[0], op.M[1], m0 + (m1 + m2), rb, cb, hw != 4, l16, grp);
     }
+}
+
+// State waves: (I + A_bb)^{-1} of one diagonal block, from A_bb in fp32, into
+// Tm as an fp16 operand. (I + A)^{-1} = (I - A)(I + A^2)(I + A^4)(I + A^8): A
+// is strictly lower triangular, so A^16 = 0 and the product is the whole
+// Neumann series (the factors commute).
+__device__ __forceinline__ void invert_block(Ops& op, int b, int l16, int grp) {
+    f32x4 A, At, ImA;
+    const float4 t4 = lds_vec<float4>(&op.Af[b][l16][4 * grp]);   // A^T in accumulator layout
+    At[0] = t4.x; At[1] = t4.y; At[2] = t4.z; At[3] = t4.w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = 4 * grp + j;
+        A[j] = op.Af[b][r][l16];
+        ImA[j] = (l16 == r ? 1.f : 0.f) - A[j];
+    }
+    const f32x4 Z = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 A2 = mprod(At, A, Z), A2t = mprod(A, At, Z);
+    const f32x4 Q1 = mprod(A2t, ImA, ImA);               // (I + A^2)(I - A)
+    const f32x4 A4 = mprod(A2t, A2, Z), A4t = mprod(A2, A2t, Z);
+    const f32x4 Q2 = mprod(A4t, Q1, Q1);                 // (I + A^4) Q1
+    const f32x4 A8t = mprod(A4, A4t, Z);
+    const f32x4 Tb = mprod(A8t, Q2, Q2);                 // (I + A^8) Q2
+    store_tile<false>(op.Tm, nullptr, Tb, 16 * b, 16 * b, false, l16, grp);
 }
 
 template <int NS>
@@ -420,7 +401,6 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
     // Zero blocks of both operand buffers, never written afterwards: kperm
     // positions 16-31 of rows 0-15 in Tm, M (hi, lo) and A10, and positions
     // 0-15 of rows 16-31 in Tm.
-    if (tid == 0) sm.pcount = 0u;
     for (int i = tid; i < 2 * C * 8; i += NT) {
         const int bsel = i / (C * 8), r = (i / 8) % C, c = 2 * (i % 8);
         const int col = kperm((r < 16 ? 16 : 0) + c);
@@ -471,11 +451,21 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
         for (int ci = 0; ci < nch; ++ci) {
             const int cs = t0 + ci * C;
             const int nv = min(C, t1 - cs);
-            const Ops& op = sm.op[ci & 1];
+            Ops& opw = sm.op[ci & 1];
+            const Ops& op = opw;
             // V of the next chunk, copied into vcur at the end of this one: the
             // loaded registers never stay pending across the loop edge, so the
             // waits for them are exact and fall after this chunk's work.
             if (ci + 1 < nch) vfetch(vnxt, ci + 1);
+            // (I + A)^{-1} of the two diagonal blocks, from the helpers' A of this
+            // chunk, for all state waves after the mid-chunk barrier. It runs on
+            // the matrix cores while the helpers' element work runs on the VALUs.
+            if (NS == 1) {
+                invert_block(opw, 0, l16, grp);
+                invert_block(opw, 1, l16, grp);
+            } else if (wave < 2) {
+                invert_block(opw, wave, l16, grp);
+            }
             // the state as a B operand: rows in kperm order, rounded to fp16
             f16x8 SBh[4];
 #pragma unroll
@@ -580,6 +570,11 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
         const int hw = wave - NS;
         const int cp = lane & 7, seg = lane >> 3;
         const uint32_t coff = 16 * hw + 2 * cp;                        // channel pair offset
+        // weights of the segment sums S0..S6 in Gamma(segment start) - Gamma_ref
+        float wpre[NSEG - 1];
+#pragma unroll
+        for (int s = 0; s < NSEG - 1; ++s)
+            wpre[s] = (s >= seg && s < NSEG / 2) ? -1.f : ((s >= NSEG / 2 && s < seg) ? 1.f : 0.f);
         HOffs offs;
 #pragma unroll
         for (int t = 0; t < SEG; ++t) {
@@ -587,15 +582,14 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
             offs.gg[t] = 2u * offs.kq[t];
         }
         offs.b = (uint32_t)(SEG * seg + (cp & 3)) * (uint32_t)a.H * 4u;
-        uint32_t ptarget = 0;
         HFetch f;
         auto prepare = [&](Ops& op, int cs) {
             const bool more = cs + C < t1;
             const int nnv = more ? min(C, t1 - cs - C) : 0;
-            factors(sm, op, f, hw, lane, more, a, base + (long long)(cs + C) * ts,
+            factors(sm, op, f, hw, lane, wpre, more, a, base + (long long)(cs + C) * ts,
                     bbase + (long long)(cs + C) * a.H, ts, offs, nnv);
             __syncthreads();   // mid-chunk barrier
-            tiles(sm, op, hw, lane, ++ptarget);
+            tiles(sm, op, hw, lane);
         };
         if (nch > 0) {
             hfetch(f, a, base + (long long)t0 * ts, bbase + (long long)t0 * a.H, ts, min(C, t1 - t0), offs);
