@@ -158,6 +158,13 @@ __device__ __forceinline__ void hfetch(HFetch& f, const FwdArgs& a, long long cb
     f.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, off.b, 0, 0));
 }
 
+// A helper lane's gated keys and queries in fp32 and its channels' decay
+// factors, kept in registers from step 1 to step 3.
+struct HStage {
+    float ka[2][SEG], qa[2][SEG], kb[2][SEG];   // k e^(G_r - G_ref), q e^(G_r - G_ref), k e^(G_ref - G_r)
+    float c1[2], c2[2];                         // e^(G_ref), e^(G_last - G_ref)
+};
+
 // Helpers, step 1: the gated factors of one chunk from the fetched registers,
 // then the fetch of the chunk after it into the same registers.
 //
@@ -168,7 +175,8 @@ __device__ __forceinline__ void hfetch(HFetch& f, const FwdArgs& a, long long cb
 // k*exp(Gamma_ref - Gamma_i) multiply to k k exp(Gamma_r - Gamma_i) for every
 // pair of tokens in the chunk. wpre holds this lane's weights of S0..S6 in
 // Gamma at its segment start minus Gamma_ref (-1, 0 or +1).
-__device__ __forceinline__ void factors(Smem& sm, Ops& op, HFetch& f, int hw, int lane, const float (&wpre)[NSEG - 1],
+__device__ __forceinline__ void factors(Smem& sm, Ops& op, HFetch& f, HStage& hs, int hw, int lane,
+                                        const float (&wpre)[NSEG - 1],
                                         bool fetch_next, const FwdArgs& a, long long nbase, long long nbeta,
                                         uint32_t ts, const HOffs& offs, int nnv) {
     const int cp = lane & 7, seg = lane >> 3;
@@ -201,7 +209,9 @@ __device__ __forceinline__ void factors(Smem& sm, Ops& op, HFetch& f, int hw, in
         const float4 v = lds_vec<float4>(&sm.segsum[hw][cp][s]);
         St[0][s] = v.x; St[1][s] = v.y; St[0][s + 1] = v.z; St[1][s + 1] = v.w;
     }
-    float d[2][SEG], c1[2], c2[2];
+    float d[2][SEG];
+    float (&c1)[2] = hs.c1;
+    float (&c2)[2] = hs.c2;
 #pragma unroll
     for (int ch = 0; ch < 2; ++ch) {
         const float* S = St[ch];
@@ -218,38 +228,49 @@ __device__ __forceinline__ void factors(Smem& sm, Ops& op, HFetch& f, int hw, in
     }
     if (seg == 0) *reinterpret_cast<float2*>(&op.gl[c0]) = make_float2(c1[0] * c2[0], c1[1] * c2[1]);
 
-    const int cpos = (c0 & ~31) | kperm(c0 & 31);
-    float kt[2][SEG];
 #pragma unroll
     for (int t = 0; t < SEG; ++t) {
-        const int r = SEG * seg + t;
-        const int so = srow(r) + c0;
-        float ka[2], qa[2], kb[2];
+        const int so = srow(SEG * seg + t) + c0;
+        float (&ka)[2][SEG] = hs.ka, (&qa)[2][SEG] = hs.qa, (&kb)[2][SEG] = hs.kb;
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
             const float e1 = ex2(d[ch][t]), e2 = ex2(-d[ch][t]);
-            ka[ch] = kv[ch][t] * e1;
-            qa[ch] = qv[ch][t] * e1;
-            kb[ch] = kv[ch][t] * e2;
-            kt[ch][t] = kb[ch] * c2[ch];
+            ka[ch][t] = kv[ch][t] * e1;
+            qa[ch][t] = qv[ch][t] * e1;
+            kb[ch][t] = kv[ch][t] * e2;
         }
         uint32_t kbh, kbl, qah, qal;
-        split_bf16x2(kb[0], kb[1], kbh, kbl);
-        split_bf16x2(qa[0], qa[1], qah, qal);
-        *reinterpret_cast<uint32_t*>(&sm.Ka[so]) = pack_bf16(ka[0], ka[1]);
+        split_bf16x2(kb[0][t], kb[1][t], kbh, kbl);
+        split_bf16x2(qa[0][t], qa[1][t], qah, qal);
+        *reinterpret_cast<uint32_t*>(&sm.Ka[so]) = pack_bf16(ka[0][t], ka[1][t]);
         *reinterpret_cast<uint32_t*>(&sm.Kbh[so]) = kbh;
         *reinterpret_cast<uint32_t*>(&sm.Kbl[so]) = kbl;
         *reinterpret_cast<uint32_t*>(&sm.Qah[so]) = qah;
         *reinterpret_cast<uint32_t*>(&sm.Qal[so]) = qal;
-        *reinterpret_cast<uint32_t*>(&op.Kg[srow(r) + cpos]) = pack_f16(ka[0] * c1[0], ka[1] * c1[1]);
-        *reinterpret_cast<uint32_t*>(&op.Qg[srow(r) + cpos]) = pack_f16(qa[0] * c1[0], qa[1] * c1[1]);
+    }
+}
+
+// Helpers, step 3: the state waves' fp16 operands K*gamma, Q*gamma and K~^T
+// of the lane's elements. Needed only from the next chunk on, so this VALU
+// work runs after the mid-chunk barrier, beside the block products.
+__device__ __forceinline__ void state_operands(Ops& op, const HStage& hs, int hw, int lane) {
+    const int cp = lane & 7, seg = lane >> 3;
+    const int c0 = 16 * hw + 2 * cp;
+    const int cpos = (c0 & ~31) | kperm(c0 & 31);
+#pragma unroll
+    for (int t = 0; t < SEG; ++t) {
+        const int so = srow(SEG * seg + t) + cpos;
+        *reinterpret_cast<uint32_t*>(&op.Kg[so]) = pack_f16(hs.ka[0][t] * hs.c1[0], hs.ka[1][t] * hs.c1[1]);
+        *reinterpret_cast<uint32_t*>(&op.Qg[so]) = pack_f16(hs.qa[0][t] * hs.c1[0], hs.qa[1][t] * hs.c1[1]);
     }
     // K~^T: the lane's four tokens are four consecutive kperm positions
     const int tp = kperm(SEG * seg);
 #pragma unroll
-    for (int ch = 0; ch < 2; ++ch)
+    for (int ch = 0; ch < 2; ++ch) {
+        const float c2 = hs.c2[ch];
         *reinterpret_cast<uint2*>(&op.KtT[c0 + ch][tp]) =
-            make_uint2(pack_f16(kt[ch][0], kt[ch][1]), pack_f16(kt[ch][2], kt[ch][3]));
+            make_uint2(pack_f16(hs.kb[ch][0] * c2, hs.kb[ch][1] * c2), pack_f16(hs.kb[ch][2] * c2, hs.kb[ch][3] * c2));
+    }
 }
 
 // X Y for 16 x 16 fp32 matrices on fp32 MFMA, from X^T and Y in accumulator
@@ -305,7 +326,7 @@ __device__ __forceinline__ void store_tile(_Float16 (*hi)[TP], _Float16 (*lo)[TP
 // A00 and A11 go to the state waves in fp32 (they invert I + A there); A10 and
 // M as fp16 operands. The zero blocks of Tm, A10 and M are written once, at
 // the kernel's start.
-__device__ __forceinline__ void tiles(Smem& sm, Ops& op, int hw, int lane) {
+__device__ __forceinline__ void tiles(Smem& sm, Ops& op, const HStage& hs, int hw, int lane) {
     const int l16 = lane & 15, grp = lane >> 4;
     if (hw <= 2) {
         // A[r][i] = beta_r (Ka_r . Kb_i): lane holds column i = l16 of rows r = 4grp + j
@@ -318,6 +339,7 @@ __device__ __forceinline__ void tiles(Smem& sm, Ops& op, int hw, int lane) {
             acc = mfma16(ka, lds_vec<bf16x8>(&sm.Kbh[srow(cb + l16) + ko]), acc);
             acc2 = mfma16(ka, lds_vec<bf16x8>(&sm.Kbl[srow(cb + l16) + ko]), acc2);
         }
+        state_operands(op, hs, hw, lane);   // VALU work while the products finish
         acc += acc2;
         if (hw < 2) {
 #pragma unroll
@@ -345,7 +367,10 @@ __device__ __forceinline__ void tiles(Smem& sm, Ops& op, int hw, int lane) {
             m1 = mfma16(qh, kl, m1);
             m2 = mfma16(ql, kh, m2);
         }
+        state_operands(op, hs, hw, lane);
         store_tile<true>(op.M[0], op.M[1], m0 + (m1 + m2), rb, cb, hw != 4, l16, grp);
+    } else {
+        state_operands(op, hs, hw, lane);
     }
 }
 
@@ -583,13 +608,14 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
         }
         offs.b = (uint32_t)(SEG * seg + (cp & 3)) * (uint32_t)a.H * 4u;
         HFetch f;
+        HStage hs;
         auto prepare = [&](Ops& op, int cs) {
             const bool more = cs + C < t1;
             const int nnv = more ? min(C, t1 - cs - C) : 0;
-            factors(sm, op, f, hw, lane, wpre, more, a, base + (long long)(cs + C) * ts,
+            factors(sm, op, f, hs, hw, lane, wpre, more, a, base + (long long)(cs + C) * ts,
                     bbase + (long long)(cs + C) * a.H, ts, offs, nnv);
             __syncthreads();   // mid-chunk barrier
-            tiles(sm, op, hw, lane);
+            tiles(sm, op, hs, hw, lane);
         };
         if (nch > 0) {
             hfetch(f, a, base + (long long)t0 * ts, bbase + (long long)t0 * a.H, ts, min(C, t1 - t0), offs);
