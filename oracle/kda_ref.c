@@ -32,16 +32,23 @@
  * handed back in without rounding; all arithmetic and the outputs are fp64.
  *
  * The only parallelism is over independent (sequence, head) pairs.
+ *
+ * gdn_ref_fwd is the same recurrence with one scalar gate per (token, head),
+ * g [B, T, H]: Gated DeltaNet, the method KDA refines by making the gate
+ * channel-wise (toolarium.ru page, section "Почему это новость про
+ * инфраструктуру"; the pages' second baseline, "gdn", in the H20 benchmark
+ * table of the same page). Every channel then decays by the same exp(g_t).
  */
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
-int kda_ref_fwd(const float* q, const float* k, const float* v, const float* g,
-                const float* beta, const int64_t* cu_seqlens, int64_t num_seqs,
-                int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
-                const double* h0, double* o, double* hT) {
+/* gate_ch: number of gate values per (token, head): K (channel-wise) or 1. */
+static int ref_fwd(const float* q, const float* k, const float* v, const float* g, int64_t gate_ch,
+                   const float* beta, const int64_t* cu_seqlens, int64_t num_seqs,
+                   int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                   const double* h0, double* o, double* hT) {
     if (K <= 0 || V <= 0 || H <= 0 || B <= 0 || T < 0) return -2;
     if (cu_seqlens && B != 1) return -2;
     const int64_t N = cu_seqlens ? num_seqs : B;
@@ -71,12 +78,12 @@ int kda_ref_fwd(const float* q, const float* k, const float* v, const float* g,
             const float* kt = k + tok * K;
             const float* qt = q + tok * K;
             const float* vt = v + tok * V;
-            const float* gt = g + tok * K;
+            const float* gt = g + tok * gate_ch;
             const double bt = (double)beta[tok];
 
-            /* decay: row c of S scales by alpha_c = exp(g_c) */
+            /* decay: row c of S scales by alpha_c = exp(g_c) (g_0 for all rows if scalar) */
             for (int64_t c = 0; c < K; ++c) {
-                const double a = exp((double)gt[c]);
+                const double a = exp((double)gt[gate_ch == 1 ? 0 : c]);
                 for (int64_t j = 0; j < V; ++j) S[c * V + j] *= a;
             }
             /* prediction error e = v - S^T k */
@@ -103,6 +110,21 @@ int kda_ref_fwd(const float* q, const float* k, const float* v, const float* g,
         free(e);
     }
     return failed ? -1 : 0;
+}
+
+int kda_ref_fwd(const float* q, const float* k, const float* v, const float* g,
+                const float* beta, const int64_t* cu_seqlens, int64_t num_seqs,
+                int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                const double* h0, double* o, double* hT) {
+    return ref_fwd(q, k, v, g, K, beta, cu_seqlens, num_seqs, B, T, H, K, V, h0, o, hT);
+}
+
+/* g: [B, T, H], one gate per (token, head). */
+int gdn_ref_fwd(const float* q, const float* k, const float* v, const float* g,
+                const float* beta, const int64_t* cu_seqlens, int64_t num_seqs,
+                int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                const double* h0, double* o, double* hT) {
+    return ref_fwd(q, k, v, g, 1, beta, cu_seqlens, num_seqs, B, T, H, K, V, h0, o, hT);
 }
 
 int kda_ref_threads(void) {

@@ -22,6 +22,8 @@ def load():
         I = ctypes.c_int64
         lib.kda_ref_fwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, P, P, P]
         lib.kda_ref_fwd.restype = ctypes.c_int
+        lib.gdn_ref_fwd.argtypes = lib.kda_ref_fwd.argtypes
+        lib.gdn_ref_fwd.restype = ctypes.c_int
         lib.kda_ref_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -41,11 +43,23 @@ def kda_ref_fwd(q, k, v, g, beta, cu_seqlens: Optional[np.ndarray] = None,
 
     Returns (o [B, T, H, V] fp64, hT [N, H, K, V] fp64 or None).
     """
+    return _run("kda_ref_fwd", q, k, v, g, beta, cu_seqlens, h0, want_state)
+
+
+def gdn_ref_fwd(q, k, v, g, beta, cu_seqlens: Optional[np.ndarray] = None,
+                h0: Optional[np.ndarray] = None, want_state: bool = True):
+    """The same fp64 recurrence with a scalar gate per (token, head): g [B, T, H]
+    (Gated DeltaNet). Other arguments and results as kda_ref_fwd."""
+    return _run("gdn_ref_fwd", q, k, v, g, beta, cu_seqlens, h0, want_state)
+
+
+def _run(fn, q, k, v, g, beta, cu_seqlens, h0, want_state):
     f = lambda x: np.ascontiguousarray(x, dtype=np.float32)
     q, k, v, g, beta = f(q), f(k), f(v), f(g), f(beta)
     B, T, H, K = q.shape
     V = v.shape[-1]
-    assert k.shape == q.shape and g.shape == q.shape and v.shape[:3] == q.shape[:3]
+    gshape = q.shape if fn == "kda_ref_fwd" else q.shape[:3]
+    assert k.shape == q.shape and g.shape == gshape and v.shape[:3] == q.shape[:3]
     assert beta.shape == (B, T, H)
     cu = None
     if cu_seqlens is not None:
@@ -59,8 +73,8 @@ def kda_ref_fwd(q, k, v, g, beta, cu_seqlens: Optional[np.ndarray] = None,
         assert h0.shape == (N, H, K, V)
     o = np.zeros((B, T, H, V), np.float64)
     hT = np.zeros((N, H, K, V), np.float64) if want_state else None
-    rc = load().kda_ref_fwd(_p(q), _p(k), _p(v), _p(g), _p(beta), _p(cu), N, B, T, H, K, V,
-                            _p(h0), _p(o), _p(hT))
+    rc = getattr(load(), fn)(_p(q), _p(k), _p(v), _p(g), _p(beta), _p(cu), N, B, T, H, K, V,
+                             _p(h0), _p(o), _p(hT))
     if rc != 0:
-        raise RuntimeError(f"kda_ref_fwd failed with code {rc}")
+        raise RuntimeError(f"{fn} failed with code {rc}")
     return o, hT

@@ -370,3 +370,68 @@ def test_bf16_rounding():
     want = np.array([1.0, 1.0, 1.0 + 2 ** -6, 1.0 + 2 ** -7, -2.5, 1.0], np.float32)
     np.testing.assert_array_equal(W.bf16_round(x), want)
     assert W.bf16_bits(np.array([1.0], np.float32))[0] == 0x3F80
+
+
+# ----------------------------------------------------------------------------- scalar gate (GDN)
+def gdn_inputs(T, H, seed, **kw):
+    q, k, v, g, beta, h0 = rand_inputs(T, H, seed, **kw)
+    return q, k, v, np.ascontiguousarray(g[..., 0]), beta, h0
+
+
+@pytest.mark.parametrize("case", ["fixed", "varlen", "h0"])
+def test_gdn_equals_kda_with_repeated_gate(case):
+    """One gate per (token, head) is KDA with that gate on every channel: the two
+    oracle entries agree bitwise (same operations in the same order)."""
+    if case == "varlen":
+        q, k, v, gs, beta, h0 = gdn_inputs(70, 3, 20, h0=True, N=3)
+        cu = np.array([0, 33, 33, 70], np.int64)
+    else:
+        q, k, v, gs, beta, h0 = gdn_inputs(45, 2, 21, B=2, h0=(case == "h0"))
+        cu = None
+    g = np.repeat(gs[..., None], q.shape[-1], axis=-1)
+    o1, h1 = oracle.gdn_ref_fwd(q, k, v, gs, beta, cu_seqlens=cu, h0=h0)
+    o2, h2 = oracle.kda_ref_fwd(q, k, v, g, beta, cu_seqlens=cu, h0=h0)
+    assert np.array_equal(o1, o2) and np.array_equal(h1, h2)
+
+
+def test_gdn_single_step_closed_form():
+    """T = 1 from h0 with a scalar gate a = exp(g): S_1 = a h0 + beta k (v - a h0^T k)^T, o = S_1^T q."""
+    q, k, v, gs, beta, h0 = gdn_inputs(1, 3, 22, h0=True)
+    o, hT = oracle.gdn_ref_fwd(q, k, v, gs, beta, h0=h0)
+    for h in range(3):
+        a = np.exp(np.float64(gs[0, 0, h]))
+        kk, qq, vv = (x[0, 0, h].astype(np.float64) for x in (k, q, v))
+        D0 = a * h0[0, h]
+        S1 = D0 + beta[0, 0, h] * np.outer(kk, vv - D0.T @ kk)
+        close(hT[0, h], S1, 1e-13, "hT")
+        close(o[0, 0, h], S1.T @ qq, 1e-13, "o")
+
+
+def test_gdn_rotation_invariance():
+    """Scalar gate: rotating q, k and h0 by an orthogonal R leaves o unchanged and maps
+    hT -> R hT. With a channel-wise gate the same rotation changes o (the pin can tell
+    the two gates apart)."""
+    T, H, K = 40, 2, 128
+    q, k, v, gs, beta, h0 = gdn_inputs(T, H, 23, h0=True)
+    R, _ = np.linalg.qr(RNG(24).standard_normal((K, K)))
+    rot = lambda x: np.einsum("ij,...j->...i", R, x.astype(np.float64))
+    h0r = np.einsum("ij,nhjv->nhiv", R, h0)
+    o, hT = oracle.gdn_ref_fwd(q, k, v, gs, beta, h0=h0)
+    o2, hT2 = oracle.gdn_ref_fwd(rot(q), rot(k), v, gs, beta, h0=h0r)
+    close(o2, o, 1e-5, "o")
+    close(hT2, np.einsum("ij,nhjv->nhiv", R, hT), 1e-5, "hT")
+    _, _, _, gc, _, _ = rand_inputs(T, H, 23)
+    oc, _ = oracle.kda_ref_fwd(q, k, v, gc, beta, h0=h0)
+    oc2, _ = oracle.kda_ref_fwd(rot(q), rot(k), v, gc, beta, h0=h0r)
+    with pytest.raises(AssertionError):
+        close(oc2, oc, 1e-5, "o (channel-wise gate)")
+
+
+def test_scalar_gate_workload():
+    cfg = W.variant("c2", T=64, H=2, gate="scalar", name="gdn")
+    inp = W.make_inputs(cfg, 0)
+    gs = inp.g_scalar()
+    assert gs.shape == (1, 64, 2) and np.all(gs <= 0) and np.all(gs >= -5)
+    base = W.make_inputs(W.variant("c2", T=64, H=2, name="kda"), 0)
+    assert np.array_equal(base.q, inp.q) and np.array_equal(base.beta, inp.beta)
+    assert np.array_equal(gs, base.g[..., 0])    # channel 0 of the same draw

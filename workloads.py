@@ -63,7 +63,7 @@ class Config:
     dtype: str = "bf16"         # dtype of q, k, v: "bf16" or "fp32"
     seq_lens: Optional[tuple] = None   # varlen mix (B must be 1); None = fixed length
     h0: bool = False            # draw an initial state per (sequence, head)
-    gate: str = "bj"            # "bj" | "mild" | "zero"   (test-only variants besides "bj")
+    gate: str = "bj"            # "bj" | "mild" | "zero" | "scalar" | "scalar_mild" (all but "bj" test-only)
     beta: str = "bj"            # "bj" | "zero" | "one"
     keys: str = "gauss"         # "gauss" | "onehot" | "same"
     note: str = ""
@@ -110,6 +110,11 @@ class Inputs:
         """bf16 bit pattern of q/k/v for bf16 configs (exact: values are already bf16)."""
         return bf16_bits(getattr(self, name))
 
+    def g_scalar(self) -> np.ndarray:
+        """The per-(token, head) gate [B, T, H] of a scalar-gate input."""
+        assert np.all(self.g == self.g[..., :1]), "gate is not scalar"
+        return np.ascontiguousarray(self.g[..., 0])
+
     def seq_bounds(self):
         """(batch row, start, end) per sequence."""
         if self.cu_seqlens is None:
@@ -155,8 +160,12 @@ def make_inputs(cfg: Config, seed: int, dtype: Optional[str] = None) -> Inputs:
     elif cfg.beta == "one":
         beta[:] = 1.0
 
+    if cfg.gate in ("scalar", "scalar_mild"):
+        # one gate per (token, head) (the Gated DeltaNet form): channel 0's draw,
+        # repeated over the channels
+        gz = np.repeat(gz[..., :1], D, axis=-1)
     g = np.maximum(-_softplus64(gz), -5.0)
-    if cfg.gate == "mild":
+    if cfg.gate in ("mild", "scalar_mild"):
         g = 0.01 * g
     elif cfg.gate == "zero":
         g = np.zeros_like(g)
