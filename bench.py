@@ -114,6 +114,52 @@ def bench_decode(args):
     }))
 
 
+def bench_gdn(args):
+    """Gated DeltaNet (one gate per token-head) at a prefill workload's shape."""
+    import numpy as np
+    import torch
+    import workloads as W
+    import gated_delta_rule_63_amd as kda
+
+    cfg = W.variant(args.config, gate="scalar", name=args.config + " scalar gate")
+    inp = W.make_inputs(cfg, args.seed)
+    dev = torch.device("cuda:0")
+    cvt = lambda x: torch.from_numpy(W.bf16_bits(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = cvt(inp.q), cvt(inp.k), cvt(inp.v)
+    gs = torch.from_numpy(inp.g_scalar()).to(dev)
+    beta = torch.from_numpy(inp.beta).to(dev)
+    cu = torch.from_numpy(inp.cu_seqlens).to(dev) if inp.cu_seqlens is not None else None
+    h0 = torch.from_numpy(inp.h0).to(dev) if inp.h0 is not None else None
+    o = torch.empty((cfg.B, cfg.T, cfg.H, 128), dtype=torch.float32, device=dev)
+    hT = torch.empty((cfg.N, cfg.H, 128, 128), dtype=torch.float32, device=dev)
+    step = lambda: kda.gdn_fwd(q, k, v, gs, beta, cu_seqlens=cu, initial_state=h0, out=o, final_state=hT)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    per_token_head = 3 * 256 + 4 + 4 + 512          # q, k, v bf16, g and beta fp32, o fp32
+    bytes_ = cfg.token_heads * per_token_head + STATE_BYTES * cfg.N * cfg.H * (1 + (1 if cfg.h0 else 0))
+    achieved = bytes_ / (ms / 1e3) / 1e9
+    print(json.dumps({
+        "metric": f"Gated DeltaNet prefill tokens/s ({cfg.name}, T={cfg.T}, H={cfg.H}, D=128 bf16)",
+        "value": cfg.B * cfg.T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: one gate per (token, head)", "global_batch": cfg.B,
+                   "seq_len": cfg.T, "heads": cfg.H, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "kda_fwd_pipe (scalar gate)",
+                     "alg_bytes_per_launch": bytes_},
+    }))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,6 +175,8 @@ def main():
     ap.add_argument("--stages", action="store_true", help="also time each staged-path kernel on its own")
     ap.add_argument("--decode", type=int, default=0, metavar="N",
                     help="time the in-place decode step for N sequences (H = 96) instead of the prefill")
+    ap.add_argument("--gdn", action="store_true",
+                    help="time the scalar-gate (Gated DeltaNet) forward at --config's shape instead")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one device-to-device copy of this many MiB at the end (counter calibration)")
     args = ap.parse_args()
@@ -137,6 +185,9 @@ def main():
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
+    if args.gdn:
+        bench_gdn(args)
+        return
     if args.decode:
         bench_decode(args)
         return

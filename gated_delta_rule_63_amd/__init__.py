@@ -16,7 +16,7 @@ import torch
 
 from ._lib import KDA_BF16, KDA_F32, Desc, KDAError, Layout, lib, status_string  # noqa: F401
 
-__all__ = ["fwd", "decode_step", "fwd_staged", "Staged", "KDAError", "status_string", "version"]
+__all__ = ["fwd", "gdn_fwd", "decode_step", "fwd_staged", "Staged", "KDAError", "status_string", "version"]
 
 D = 128
 
@@ -36,7 +36,7 @@ def _desc(q: torch.Tensor, cu_seqlens: Optional[torch.Tensor]) -> Desc:
     return Desc(B, T, H, K, K, N, dt, KDA_F32, None, 0)
 
 
-def _check_inputs(q, k, v, g, beta, cu_seqlens):
+def _check_inputs(q, k, v, g, beta, cu_seqlens, scalar_gate=False):
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous device tensor")
@@ -44,8 +44,10 @@ def _check_inputs(q, k, v, g, beta, cu_seqlens):
         raise ValueError("q, k, v must share a dtype")
     if g.dtype != torch.float32 or beta.dtype != torch.float32:
         raise ValueError("g and beta must be float32")
-    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape or g.shape != q.shape:
-        raise ValueError("q, k, v, g must all be [B, T, H, 128]")
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must all be [B, T, H, 128]")
+    if g.shape != (q.shape[:3] if scalar_gate else q.shape):
+        raise ValueError("g must be [B, T, H]" if scalar_gate else "g must be [B, T, H, 128]")
     if beta.shape != q.shape[:3]:
         raise ValueError("beta must be [B, T, H]")
     if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda):
@@ -63,7 +65,24 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
     Returns (o fp32 [B, T, H, 128], hT or None). Tensors must be contiguous and on
     one GPU; q, k, v share a dtype (bf16 or fp32); g and beta are fp32.
     """
-    _check_inputs(q, k, v, g, beta, cu_seqlens)
+    return _forward("kda_fwd", q, k, v, g, beta, cu_seqlens, initial_state, output_final_state,
+                    out, final_state, stream)
+
+
+def gdn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+            cu_seqlens: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
+            output_final_state: bool = True, out: Optional[torch.Tensor] = None,
+            final_state: Optional[torch.Tensor] = None,
+            stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Gated DeltaNet forward (kda_gdn_fwd): as fwd, but g is one fp32 log-decay per
+    (token, head), [B, T, H]."""
+    return _forward("kda_gdn_fwd", q, k, v, g, beta, cu_seqlens, initial_state, output_final_state,
+                    out, final_state, stream)
+
+
+def _forward(entry, q, k, v, g, beta, cu_seqlens, initial_state, output_final_state, out, final_state,
+             stream):
+    _check_inputs(q, k, v, g, beta, cu_seqlens, scalar_gate=(entry == "kda_gdn_fwd"))
     d = _desc(q, cu_seqlens)
     B, T, H, _ = q.shape
     if initial_state is not None:
@@ -76,10 +95,10 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
         hT = final_state if final_state is not None else torch.empty(
             (d.num_seqs, H, D, D), dtype=torch.float32, device=q.device)
     s = (stream or torch.cuda.current_stream(q.device)).cuda_stream
-    rc = lib().kda_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
-                       _ptr(initial_state), _ptr(o), _ptr(hT), ctypes.byref(d), ctypes.c_void_p(s))
+    rc = getattr(lib(), entry)(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                               _ptr(initial_state), _ptr(o), _ptr(hT), ctypes.byref(d), ctypes.c_void_p(s))
     if rc != 0:
-        raise KDAError(rc, "kda_fwd")
+        raise KDAError(rc, entry)
     return o, hT
 
 

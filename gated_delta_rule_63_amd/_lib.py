@@ -12,7 +12,7 @@ STATUS = {0: "KDA_OK", -1: "KDA_ERR_NULL", -2: "KDA_ERR_SHAPE", -3: "KDA_ERR_UNS
           -4: "KDA_ERR_DTYPE", -5: "KDA_ERR_WORKSPACE", -6: "KDA_ERR_HIP"}
 
 # every symbol include/kda.h declares
-EXPORTS = ["kda_status_string", "kda_version", "kda_fwd_check", "kda_fwd", "kda_decode_step", "kda_staged_layout",
+EXPORTS = ["kda_status_string", "kda_version", "kda_fwd_check", "kda_fwd", "kda_gdn_fwd", "kda_decode_step", "kda_staged_layout",
            "kda_fwd_workspace_size", "kda_stage_chunk_map", "kda_stage_gate_scan", "kda_stage_intra",
            "kda_stage_recurrence", "kda_stage_output", "kda_fwd_staged"]
 
@@ -54,6 +54,8 @@ def lib():
         L.kda_fwd_check.restype = ctypes.c_int
         L.kda_fwd.argtypes = [P] * 9 + [ctypes.POINTER(Desc), P]
         L.kda_fwd.restype = ctypes.c_int
+        L.kda_gdn_fwd.argtypes = [P] * 9 + [ctypes.POINTER(Desc), P]
+        L.kda_gdn_fwd.restype = ctypes.c_int
         L.kda_decode_step.argtypes = [P] * 8 + [ctypes.POINTER(Desc), P]
         L.kda_decode_step.restype = ctypes.c_int
         L.kda_fwd_workspace_size.argtypes = [ctypes.POINTER(Desc)]

@@ -51,6 +51,23 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Compute units of the current device, read once per device (the attribute
+// cannot change while the process runs; concurrent first calls store the
+// same value).
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 kda::FwdArgs fwd_args(const void* q, const void* k, const void* v, const float* g, const float* beta,
                       const int32_t* cu_seqlens, const float* h0, void* o, float* hT, const kda_desc_t* d) {
     kda::FwdArgs a;
@@ -68,7 +85,22 @@ kda::FwdArgs fwd_args(const void* q, const void* k, const void* v, const float* 
     a.H = d->H;
     a.N = d->num_seqs;
     a.nchains = d->num_seqs * d->H;
+    a.scalar_gate = 0;
     return a;
+}
+
+// Chooses the kernel for a forward pass (kda_fwd and kda_gdn_fwd).
+kda_status_t run_fwd(const kda::FwdArgs& a, const kda_desc_t* desc, const void* o, const float* h0,
+                     const float* hT, bool varlen, void* stream) {
+    if (a.nchains == 0) return KDA_OK;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool f32 = desc->in_dtype == KDA_F32;
+    hipError_t e;
+    if (desc->T == 1 && !varlen && aligned16(o) && aligned16(h0) && aligned16(hT))
+        e = kda::launch_decode(a, f32, s);   // one token per sequence: a single recurrence step
+    else
+        e = f32 ? kda::launch_fwd_serial(a, true, s) : kda::launch_fwd_pipe(a, device_cus(), s);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 // Layout of the staged path's workspace. Whether the descriptor is varlen is
@@ -132,22 +164,6 @@ kda_status_t stage_args(const kda_desc_t* d, const int32_t* cu, kda::StageArgs* 
 
 kda_status_t hip_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
 
-// Compute units of the current device, read once per device (the attribute
-// cannot change while the process runs; concurrent first calls store the
-// same value).
-int device_cus() {
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-    if (dev < 64) {
-        const int c = cache[dev].load(std::memory_order_relaxed);
-        if (c > 0) return c;
-    }
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
-    return n;
-}
 
 }  // namespace
 
@@ -182,15 +198,17 @@ kda_status_t kda_fwd(const void* q, const void* k, const void* v, const float* g
     const kda_status_t st = check(q, k, v, g, beta, cu_seqlens, o, desc);
     if (st != KDA_OK) return st;
     const kda::FwdArgs a = fwd_args(q, k, v, g, beta, cu_seqlens, h0, o, hT, desc);
-    if (a.nchains == 0) return KDA_OK;
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool f32 = desc->in_dtype == KDA_F32;
-    hipError_t e;
-    if (desc->T == 1 && !cu_seqlens && aligned16(o) && aligned16(h0) && aligned16(hT))
-        e = kda::launch_decode(a, f32, s);   // one token per sequence: a single recurrence step
-    else
-        e = f32 ? kda::launch_fwd_serial(a, true, s) : kda::launch_fwd_pipe(a, device_cus(), s);
-    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    return run_fwd(a, desc, o, h0, hT, cu_seqlens != nullptr, stream);
+}
+
+kda_status_t kda_gdn_fwd(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const int32_t* cu_seqlens, const float* h0, void* o,
+                         float* hT, const kda_desc_t* desc, void* stream) {
+    const kda_status_t st = check(q, k, v, g, beta, cu_seqlens, o, desc);
+    if (st != KDA_OK) return st;
+    kda::FwdArgs a = fwd_args(q, k, v, g, beta, cu_seqlens, h0, o, hT, desc);
+    a.scalar_gate = 1;
+    return run_fwd(a, desc, o, h0, hT, cu_seqlens != nullptr, stream);
 }
 
 kda_status_t kda_decode_step(const void* q, const void* k, const void* v, const float* g,

@@ -37,7 +37,7 @@ __global__ __launch_bounds__(NT) void kda_decode_kernel(FwdArgs a) {
     if (t < D) {
         sk[t] = ld_in<F32>(a.k, tok + t);
         sq[t] = ld_in<F32>(a.q, tok + t);
-        sgam[t] = expf(a.g[tok + t]);
+        sgam[t] = expf(a.scalar_gate ? a.g[(long long)n * a.H + h] : a.g[tok + t]);
     }
     // this thread's block of the state
     float4 s[16];

@@ -139,19 +139,26 @@ struct HFetch {
     float beta;
 };
 // Byte offsets of those elements within a chunk of k or q, of g, and of beta.
+// With a scalar gate (SG) g has beta's layout and gg[t] is token t's offset there.
 struct HOffs {
     uint32_t kq[SEG], gg[SEG], b;
 };
 
+template <bool SG>
 __device__ __forceinline__ void hfetch(HFetch& f, const FwdArgs& a, long long cbase, long long cbeta,
                                        uint32_t ts, int nv, const HOffs& off) {
     const auto rk = chunk_rsrc(a.k, cbase, 2, nv, ts, D);
     const auto rq = chunk_rsrc(a.q, cbase, 2, nv, ts, D);
-    const auto rg = chunk_rsrc(a.g, cbase, 4, nv, ts, D);
+    const auto rg = SG ? chunk_rsrc(a.g, cbeta, 4, nv, (uint32_t)a.H, 1) : chunk_rsrc(a.g, cbase, 4, nv, ts, D);
     const auto rb = chunk_rsrc(a.beta, cbeta, 4, nv, (uint32_t)a.H, 1);
 #pragma unroll
     for (int t = 0; t < SEG; ++t) {
-        f.g[t] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rg, off.gg[t], 0, 0));
+        if constexpr (SG) {
+            const float gs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, off.gg[t], 0, 0));
+            f.g[t] = make_float2(gs, gs);
+        } else {
+            f.g[t] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rg, off.gg[t], 0, 0));
+        }
         f.k[t] = __builtin_amdgcn_raw_buffer_load_b32(rk, off.kq[t], 0, 0);
         f.q[t] = __builtin_amdgcn_raw_buffer_load_b32(rq, off.kq[t], 0, 0);
     }
@@ -175,6 +182,7 @@ struct HStage {
 // k*exp(Gamma_ref - Gamma_i) multiply to k k exp(Gamma_r - Gamma_i) for every
 // pair of tokens in the chunk. wpre holds this lane's weights of S0..S6 in
 // Gamma at its segment start minus Gamma_ref (-1, 0 or +1).
+template <bool SG>
 __device__ __forceinline__ void factors(Smem& sm, Ops& op, HFetch& f, HStage& hs, int hw, int lane,
                                         const float (&wpre)[NSEG - 1],
                                         bool fetch_next, const FwdArgs& a, long long nbase, long long nbeta,
@@ -197,7 +205,7 @@ __device__ __forceinline__ void factors(Smem& sm, Ops& op, HFetch& f, HStage& hs
     sm.segsum[hw][cp][seg] = make_float2(r0, r1);
     if (hw == 0 && cp < SEG) op.beta[SEG * seg + cp] = f.beta;
     // the fetched registers are consumed: fetch the chunk after this one
-    if (fetch_next) hfetch(f, a, nbase, nbeta, ts, nnv, offs);
+    if (fetch_next) hfetch<SG>(f, a, nbase, nbeta, ts, nnv, offs);
 
     // all eight segment sums of this channel pair (written by this wave)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -398,7 +406,7 @@ __device__ __forceinline__ void invert_block(Ops& op, int b, int l16, int grp) {
     store_tile<false>(op.Tm, nullptr, Tb, 16 * b, 16 * b, false, l16, grp);
 }
 
-template <int NS>
+template <int NS, bool SG>
 __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
     constexpr int NT = Split<NS>::NT, VB = Split<NS>::VB, P = Split<NS>::P;
     __shared__ Smem sm;
@@ -604,7 +612,7 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
 #pragma unroll
         for (int t = 0; t < SEG; ++t) {
             offs.kq[t] = ((uint32_t)(SEG * seg + t) * ts + coff) * 2u;
-            offs.gg[t] = 2u * offs.kq[t];
+            offs.gg[t] = SG ? (uint32_t)(SEG * seg + t) * (uint32_t)a.H * 4u : 2u * offs.kq[t];
         }
         offs.b = (uint32_t)(SEG * seg + (cp & 3)) * (uint32_t)a.H * 4u;
         HFetch f;
@@ -612,13 +620,13 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
         auto prepare = [&](Ops& op, int cs) {
             const bool more = cs + C < t1;
             const int nnv = more ? min(C, t1 - cs - C) : 0;
-            factors(sm, op, f, hs, hw, lane, wpre, more, a, base + (long long)(cs + C) * ts,
+            factors<SG>(sm, op, f, hs, hw, lane, wpre, more, a, base + (long long)(cs + C) * ts,
                     bbase + (long long)(cs + C) * a.H, ts, offs, nnv);
             __syncthreads();   // mid-chunk barrier
             tiles(sm, op, hs, hw, lane);
         };
         if (nch > 0) {
-            hfetch(f, a, base + (long long)t0 * ts, bbase + (long long)t0 * a.H, ts, min(C, t1 - t0), offs);
+            hfetch<SG>(f, a, base + (long long)t0 * ts, bbase + (long long)t0 * a.H, ts, min(C, t1 - t0), offs);
             prepare(sm.op[0], t0);
         }
         __syncthreads();
@@ -647,12 +655,16 @@ hipError_t launch_fwd_pipe(const FwdArgs& a, int cus, hipStream_t stream) {
     const int ns = pipe_state_waves(a.nchains, cus);
     const int grid = pipe_workgroups(a.nchains, ns);
     if (grid == 0) return hipSuccess;
-    if (ns == 1)
-        hipLaunchKernelGGL(pipe::kda_fwd_pipe<1>, dim3(grid), dim3(pipe::Split<1>::NT), 0, stream, a);
-    else if (ns == 2)
-        hipLaunchKernelGGL(pipe::kda_fwd_pipe<2>, dim3(grid), dim3(pipe::Split<2>::NT), 0, stream, a);
-    else
-        hipLaunchKernelGGL(pipe::kda_fwd_pipe<4>, dim3(grid), dim3(pipe::Split<4>::NT), 0, stream, a);
+    const dim3 g3(grid);
+    if (a.scalar_gate) {
+        if (ns == 1) hipLaunchKernelGGL((pipe::kda_fwd_pipe<1, true>), g3, dim3(pipe::Split<1>::NT), 0, stream, a);
+        else if (ns == 2) hipLaunchKernelGGL((pipe::kda_fwd_pipe<2, true>), g3, dim3(pipe::Split<2>::NT), 0, stream, a);
+        else hipLaunchKernelGGL((pipe::kda_fwd_pipe<4, true>), g3, dim3(pipe::Split<4>::NT), 0, stream, a);
+    } else {
+        if (ns == 1) hipLaunchKernelGGL((pipe::kda_fwd_pipe<1, false>), g3, dim3(pipe::Split<1>::NT), 0, stream, a);
+        else if (ns == 2) hipLaunchKernelGGL((pipe::kda_fwd_pipe<2, false>), g3, dim3(pipe::Split<2>::NT), 0, stream, a);
+        else hipLaunchKernelGGL((pipe::kda_fwd_pipe<4, false>), g3, dim3(pipe::Split<4>::NT), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

@@ -110,7 +110,12 @@ __device__ __forceinline__ void fetch(Fetch<F32>& f, const FwdArgs& a, long long
         const int rr = 8 * qq + t;
         const uint32_t o = of.gk + (uint32_t)t * ts;
         if (rr < nv) {
-            f.g[t] = *reinterpret_cast<const float2*>(gch + o);
+            if (a.scalar_gate) {
+                const float gs = a.g[cbeta + (uint32_t)rr * (uint32_t)a.H];
+                f.g[t] = make_float2(gs, gs);
+            } else {
+                f.g[t] = *reinterpret_cast<const float2*>(gch + o);
+            }
             if constexpr (F32) {
                 f.k[t] = *reinterpret_cast<const float2*>(static_cast<const float*>(a.k) + cbase + o);
                 f.q[t] = *reinterpret_cast<const float2*>(static_cast<const float*>(a.q) + cbase + o);

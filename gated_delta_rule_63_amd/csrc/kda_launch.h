@@ -11,7 +11,7 @@ struct FwdArgs {
     const void* q;
     const void* k;
     const void* v;
-    const float* g;
+    const float* g;      // [B, T, H, K], or [B, T, H] when scalar_gate
     const float* beta;
     const int32_t* cu;   // device cu_seqlens or nullptr
     const float* h0;     // nullptr: zero initial state
@@ -19,6 +19,7 @@ struct FwdArgs {
     float* hT;           // nullptr: final state not written
     int B, T, H, N;
     int nchains;         // N * H
+    int scalar_gate;     // 1: one gate per (token, head) (Gated DeltaNet)
 };
 
 // One phase at a time (both input dtypes); used for fp32 inputs.

@@ -102,6 +102,23 @@ kda_status_t kda_fwd(const void* q, const void* k, const void* v, const float* g
                      void* o, float* hT, const kda_desc_t* desc, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Gated DeltaNet forward: the same recurrence with one scalar gate per
+ * (token, head) instead of one per channel. KDA is presented as Gated DeltaNet
+ * refined with channel-wise gating, and the pages benchmark FlashKDA against a
+ * "gdn" kernel (toolarium.ru page, section "Почему это новость про
+ * инфраструктуру" and its H20 benchmark table).
+ *
+ *     S_t = (I - beta_t k_t k_t^T) exp(g_t) S_{t-1} + beta_t k_t v_t^T,  o_t = S_t^T q_t
+ *
+ * Arguments, layouts, aliasing, routing and errors exactly as kda_fwd, except
+ *     g  [B, T, H] fp32, one natural-log decay per (token, head), in [-5, 0].
+ * The result equals kda_fwd with g repeated over the 128 channels, bit for
+ * bit; the gate costs 4 bytes per token-head instead of 512. */
+kda_status_t kda_gdn_fwd(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const int32_t* cu_seqlens, const float* h0,
+                         void* o, float* hT, const kda_desc_t* desc, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Decode step: one new token for each of N sequences, i.e. one step of the
  * recurrence above per (sequence, head), applied to a state carried over from
  * a prefill (the pages list decode as the next, not yet tuned, part of the
