@@ -474,6 +474,10 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
         // compiler cannot prove them done inside the chunk loop and waits there
         // for every outstanding load, including the next chunk's prefetch.
         __builtin_amdgcn_s_waitcnt(0x0F70);
+        // The state waves' dependent chain (solve, output, state update) sets
+        // the length of each chunk's second phase, while the helpers have slack
+        // there: the state waves issue first when both are ready.
+        __builtin_amdgcn_s_setprio(2);
         if (nch > 0) {
             vfetch(vnxt, 0);
 #pragma unroll
