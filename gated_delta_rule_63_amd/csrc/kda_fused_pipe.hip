@@ -526,13 +526,19 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
                     Ot[t] = mfma16(lds_vec<f16x8>(&op.Qg[off]), SBh[kk], Ot[t]);
                 }
             }
+            // beta and A10 of this chunk were written before the last barrier:
+            // read them now, so the solve after the barrier starts without an
+            // LDS round trip (T is written in this phase and is read after it).
+            const float4 bt0 = lds_vec<float4>(&op.beta[4 * grp]), bt1 = lds_vec<float4>(&op.beta[16 + 4 * grp]);
+            const f16x8 ah = lds_vec<f16x8>(&op.A10[l16][8 * grp]);
             __syncthreads();   // mid-chunk: the helpers' factors of chunk ci+1 are written
+            const float bts[2][4] = {{bt0.x, bt0.y, bt0.z, bt0.w}, {bt1.x, bt1.y, bt1.z, bt1.w}};
             float be[2][4];
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    be[t][j] = op.beta[16 * t + 4 * grp + j] * (__uint_as_float(vcur[4 * t + j] << 16) - Pt[t][j]);
+                    be[t][j] = bts[t][j] * (__uint_as_float(vcur[4 * t + j] << 16) - Pt[t][j]);
             // Delta0 = T00 bE0 (two-term fp16 operand; slots of sub-block 1 are zero)
             uint32_t bh[4] = {0u, 0u, 0u, 0u}, bl[4] = {0u, 0u, 0u, 0u};
             split_f16x2(be[0][0], be[0][1], bh[0], bl[0]);
@@ -549,7 +555,6 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
             // Delta1 = T11 (bE1 - A10 Delta0)
             f32x4 X = {0.f, 0.f, 0.f, 0.f};
             {
-                const f16x8 ah = lds_vec<f16x8>(&op.A10[l16][8 * grp]);
                 X = mfma16(ah, __builtin_bit_cast(f16x8, dh), X);
                 X = mfma16(ah, __builtin_bit_cast(f16x8, dl), X);
             }
