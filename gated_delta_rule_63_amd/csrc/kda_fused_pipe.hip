@@ -53,6 +53,7 @@ constexpr int SHIFT = 16;      // extra 2-byte elements before each further grou
 constexpr int LD32 = D + 4;    // row pitch of an fp32 [token][channel] array
 constexpr int TP = C + 8;      // row pitch of a 2-byte [row][32] array
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr int MAX_RANKED = 64;  // varlen batches up to this many sequences run longest first
 static_assert(NH * 16 == D && NSEG * 8 == 64, "helper lanes: 8 channel pairs x 8 segments per wave");
 
 // Row r of a [token][channel] 2-byte array. Each group of eight rows starts 32
@@ -114,6 +115,7 @@ struct alignas(16) Smem {
     __bf16 Qah[ROWS32];             // q * exp(Gamma_r - Gamma_ref) = Qah + Qal
     __bf16 Qal[ROWS32];
     float2 segsum[NH][8][NSEG];     // per helper wave: segment sums of each channel pair
+    int seq;                        // the sequence this workgroup runs (varlen)
 };
 
 // x = hi + lo for a pair of floats: hi is x cut to bf16 (its upper 16 bits, so
@@ -421,7 +423,24 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
     const int vblk = rest % P;
     const int chain = (rest / P) * 8 + xcd;
     if (chain >= a.nchains) return;
-    const int n = chain / a.H, h = chain % a.H;
+    const int h = chain % a.H;
+    int n = chain / a.H;
+    if (a.cu && a.N <= MAX_RANKED) {
+        // Longest sequences first: workgroups are dispatched roughly in id
+        // order, so the long chains start early and the short ones fill in
+        // behind them. Sequence rank = number of longer ones (ties by index).
+        if (tid < a.N) {
+            const int len = a.cu[tid + 1] - a.cu[tid];
+            int rank = 0;
+            for (int m = 0; m < a.N; ++m) {
+                const int lm = a.cu[m + 1] - a.cu[m];
+                rank += (lm > len || (lm == len && m < tid)) ? 1 : 0;
+            }
+            if (rank == n) sm.seq = tid;
+        }
+        __syncthreads();
+        n = sm.seq;
+    }
     int row, t0, t1;
     if (a.cu) { row = 0; t0 = a.cu[n]; t1 = a.cu[n + 1]; }
     else      { row = n; t0 = 0;       t1 = a.T; }
