@@ -222,8 +222,11 @@ __device__ __forceinline__ void factors(Smem& sm, Ops& op, HFetch& f, HStage& hs
     float d[2][SEG];
     float (&c1)[2] = hs.c1;
     float (&c2)[2] = hs.c2;
+    // A scalar gate gives both channels of the lane the same factors: form
+    // them once (the same operations, so the values are the channel-wise ones).
+    constexpr int NCH = SG ? 1 : 2;
 #pragma unroll
-    for (int ch = 0; ch < 2; ++ch) {
+    for (int ch = 0; ch < NCH; ++ch) {
         const float* S = St[ch];
         const float ref = (S[0] + S[1]) + (S[2] + S[3]);
         const float last = (S[4] + S[5]) + (S[6] + S[7]);      // Gamma_last - Gamma_ref
@@ -236,15 +239,29 @@ __device__ __forceinline__ void factors(Smem& sm, Ops& op, HFetch& f, HStage& hs
 #pragma unroll
         for (int t = 0; t < SEG; ++t) d[ch][t] = fmaf(L[ch][t], LOG2E, m2);
     }
+    if constexpr (SG) {
+        c1[1] = c1[0];
+        c2[1] = c2[0];
+    }
     if (seg == 0) *reinterpret_cast<float2*>(&op.gl[c0]) = make_float2(c1[0] * c2[0], c1[1] * c2[1]);
 
 #pragma unroll
     for (int t = 0; t < SEG; ++t) {
         const int so = srow(SEG * seg + t) + c0;
         float (&ka)[2][SEG] = hs.ka, (&qa)[2][SEG] = hs.qa, (&kb)[2][SEG] = hs.kb;
+        float e1s[2], e2s[2];
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch) {
+            e1s[ch] = ex2(d[ch][t]);
+            e2s[ch] = ex2(-d[ch][t]);
+        }
+        if constexpr (SG) {
+            e1s[1] = e1s[0];
+            e2s[1] = e2s[0];
+        }
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
-            const float e1 = ex2(d[ch][t]), e2 = ex2(-d[ch][t]);
+            const float e1 = e1s[ch], e2 = e2s[ch];
             ka[ch][t] = kv[ch][t] * e1;
             qa[ch][t] = qv[ch][t] * e1;
             kb[ch][t] = kv[ch][t] * e2;
