@@ -50,7 +50,6 @@ constexpr int SEG = 4;         // tokens per helper lane
 constexpr int NSEG = C / SEG;  // segments per chunk (lanes 8*seg + cp)
 constexpr int LDP = D + 8;     // row pitch of a 2-byte [token][channel] array
 constexpr int SHIFT = 16;      // extra 2-byte elements before each further group of eight rows
-constexpr int LD32 = D + 4;    // row pitch of an fp32 [token][channel] array
 constexpr int TP = C + 8;      // row pitch of a 2-byte [row][32] array
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr int MAX_RANKED = 64;  // varlen batches up to this many sequences run longest first
