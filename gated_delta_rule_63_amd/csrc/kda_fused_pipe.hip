@@ -15,8 +15,8 @@
 //     workgroup synchronisation. Before the mid-chunk barrier the lanes form
 //     every gated factor of their eight elements (VALU work); after it the
 //     helpers build the gated K K^T blocks (A) and the gated Q K^T blocks (M)
-//     on bf16 MFMA, writing the state waves' operands into the other half of
-//     a double-buffered LDS area.
+//     on bf16 MFMA and form the state waves' fp16 operands, writing them into
+//     the other half of a double-buffered LDS area.
 // So the element work of chunk i+1 overlaps the inversion and the products
 // with the old state of chunk i, and the block products of chunk i+1 overlap
 // the solve and state update of chunk i. Two workgroup barriers per chunk: the
