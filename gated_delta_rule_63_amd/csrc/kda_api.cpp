@@ -86,7 +86,64 @@ kda::FwdArgs fwd_args(const void* q, const void* k, const void* v, const float* 
     a.N = d->num_seqs;
     a.nchains = d->num_seqs * d->H;
     a.scalar_gate = 0;
+    a.ntasks = 0;
     return a;
+}
+
+constexpr int kMinSlice = 4096;   // tokens per slice before a chain is cut into three
+
+// Few long chains (fixed-length, bf16): the chip holds far more workgroups
+// than the chains fill, and each chain is a long sequential walk. Cut every
+// chain into three slices of whole chunks: pass 1 runs slice 0 for real and,
+// at the same time, slice 1 from zero and from the identity (its affine map);
+// a combine kernel forms slice 2's start state; pass 2 reruns slice 1 and runs
+// slice 2 from their true start states. The critical path shrinks to two
+// thirds at the price of one extra slice of work per chain.
+bool use_slices(const kda::FwdArgs& a, const kda_desc_t* d, bool varlen, int cus) {
+    return d->in_dtype == KDA_BF16 && !varlen && d->T >= 3 * kMinSlice && 6LL * a.nchains <= cus;
+}
+
+hipError_t run_slices(const kda::FwdArgs& a, const kda_desc_t* d, int cus, hipStream_t s) {
+    const size_t per = (size_t)a.nchains * 128 * 128;
+    const size_t bytes = 4 * per * sizeof(float);
+    void* ws = nullptr;
+    bool owned = false;
+    if (d->workspace && d->workspace_bytes >= bytes) {
+        ws = d->workspace;
+    } else {
+        if (hipMallocAsync(&ws, bytes, s) != hipSuccess) {
+            (void)hipGetLastError();
+            return kda::launch_fwd_pipe(a, cus, s);   // no room: one pass over whole chains
+        }
+        owned = true;
+    }
+    float* S1 = static_cast<float*>(ws);   // state after slice 0
+    float* R1 = S1 + per;                   // slice 1 from zero
+    float* P1 = R1 + per;                   // slice 1's transition map
+    float* S2 = P1 + per;                   // state after slice 1
+    const int T = d->T;
+    const int s1 = (T / 3) / 32 * 32, s2 = (2 * T / 3) / 32 * 32;
+    kda::FwdArgs p1 = a;
+    p1.ntasks = 3;
+    p1.nchains = 3 * a.nchains;
+    p1.task[0] = {0, s1, a.h0, S1, 0};
+    p1.task[1] = {s1, s2, nullptr, R1, kda::TASK_NO_OUTPUT};
+    p1.task[2] = {s1, s2, nullptr, P1, kda::TASK_NO_OUTPUT | kda::TASK_ZERO_V | kda::TASK_IDENTITY_H0};
+    hipError_t e = kda::launch_fwd_pipe(p1, cus, s);
+    if (e == hipSuccess) e = kda::launch_affine_combine(P1, S1, R1, S2, a.nchains, s);
+    if (e == hipSuccess) {
+        kda::FwdArgs p2 = a;
+        p2.ntasks = 2;
+        p2.nchains = 2 * a.nchains;
+        p2.task[0] = {s1, s2, S1, nullptr, 0};
+        p2.task[1] = {s2, T, S2, a.hT, 0};
+        e = kda::launch_fwd_pipe(p2, cus, s);
+    }
+    if (owned) {
+        const hipError_t ef = hipFreeAsync(ws, s);
+        if (e == hipSuccess) e = ef;
+    }
+    return e;
 }
 
 // Chooses the kernel for a forward pass (kda_fwd and kda_gdn_fwd).
@@ -96,10 +153,13 @@ kda_status_t run_fwd(const kda::FwdArgs& a, const kda_desc_t* desc, const void* 
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const bool f32 = desc->in_dtype == KDA_F32;
     hipError_t e;
+    const int cus = device_cus();
     if (desc->T == 1 && !varlen && aligned16(o) && aligned16(h0) && aligned16(hT))
         e = kda::launch_decode(a, f32, s);   // one token per sequence: a single recurrence step
+    else if (use_slices(a, desc, varlen, cus))
+        e = run_slices(a, desc, cus, s);
     else
-        e = f32 ? kda::launch_fwd_serial(a, true, s) : kda::launch_fwd_pipe(a, device_cus(), s);
+        e = f32 ? kda::launch_fwd_serial(a, true, s) : kda::launch_fwd_pipe(a, cus, s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -439,8 +439,10 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
     const int vblk = rest % P;
     const int chain = (rest / P) * 8 + xcd;
     if (chain >= a.nchains) return;
+    const int NH_ = a.N * a.H;
+    const int task = a.ntasks > 0 ? chain / NH_ : 0;
     const int h = chain % a.H;
-    int n = chain / a.H;
+    int n = (chain % NH_) / a.H;
     if (a.cu && a.N <= MAX_RANKED) {
         // Longest sequences first: workgroups are dispatched roughly in id
         // order, so the long chains start early and the short ones fill in
@@ -455,11 +457,34 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
             if (rank == n) sm.seq = tid;
         }
         __syncthreads();
-        n = sm.seq;
+        n = __builtin_amdgcn_readfirstlane(sm.seq);
     }
     int row, t0, t1;
+    const float* h0p = a.h0;
+    float* hTp = a.hT;
+    int tflags = 0;
     if (a.cu) { row = 0; t0 = a.cu[n]; t1 = a.cu[n + 1]; }
     else      { row = n; t0 = 0;       t1 = a.T; }
+    if (a.ntasks > 0) {
+        // The task index is uniform, but a dynamic index into the argument
+        // block is not seen as such: make the fields scalar again, or every
+        // buffer resource built from them would need a waterfall loop.
+        const FwdTask& tk = a.task[task];
+        t0 = __builtin_amdgcn_readfirstlane(tk.t_begin);
+        t1 = __builtin_amdgcn_readfirstlane(tk.t_end);
+        tflags = __builtin_amdgcn_readfirstlane(tk.flags);
+        const auto uptr = [](const void* p) {
+            const uint64_t u = reinterpret_cast<uint64_t>(p);
+            const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+            const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+            return ((uint64_t)hi << 32) | lo;
+        };
+        h0p = reinterpret_cast<const float*>(uptr(tk.h0));
+        hTp = reinterpret_cast<float*>(uptr(tk.hT));
+    }
+    // uniform per workgroup: keep them scalar (buffer resources are built from them)
+    t0 = __builtin_amdgcn_readfirstlane(t0);
+    t1 = __builtin_amdgcn_readfirstlane(t1);
     const int nch = (t1 - t0 + C - 1) / C;
     const uint32_t ts = (uint32_t)a.H * D;
     const long long base = (long long)row * a.T * ts + (long long)h * D;
@@ -496,7 +521,8 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
         // bf16 bits (zero past the chunk's end).
         auto vfetch = [&](uint32_t* dst, int cidx) {
             const int cs = t0 + cidx * C;
-            const auto rv = chunk_rsrc(a.v, base + (long long)cs * ts, 2, min(C, t1 - cs), ts, D);
+            // an empty resource reads zeros (a slice run with v = 0)
+            const auto rv = chunk_rsrc(a.v, base + (long long)cs * ts, 2, (tflags & TASK_ZERO_V) ? 0 : min(C, t1 - cs), ts, D);
 #pragma unroll
             for (int i = 0; i < 8; ++i) dst[i] = __builtin_amdgcn_raw_buffer_load_b16(rv, voff[i], 0, 0);
         };
@@ -504,7 +530,8 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
         for (int m = 0; m < 8; ++m)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                S[m][j] = a.h0 ? a.h0[sbase + (uint32_t)(16 * m + 4 * grp + j) * D + vc] : 0.f;
+                S[m][j] = (tflags & TASK_IDENTITY_H0) ? (16 * m + 4 * grp + j == vc ? 1.f : 0.f)
+                          : h0p ? h0p[sbase + (uint32_t)(16 * m + 4 * grp + j) * D + vc] : 0.f;
         // Complete the h0 loads here (s_waitcnt vmcnt(0)): otherwise the
         // compiler cannot prove them done inside the chunk loop and waits there
         // for every outstanding load, including the next chunk's prefetch.
@@ -606,7 +633,8 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
             split_f16x2(D1[2], D1[3], dh[3], dl[3]);
             const f16x8 DBh = __builtin_bit_cast(f16x8, dh), DBl = __builtin_bit_cast(f16x8, dl);
             // O = (Q*gamma) S + M Delta (rows past the chunk's end are dropped)
-            const auto ro = chunk_rsrc(a.o, base + (long long)cs * ts, 4, nv, ts, D);
+            // an empty resource drops the stores (a slice run for its state only)
+            const auto ro = chunk_rsrc(a.o, base + (long long)cs * ts, 4, (tflags & TASK_NO_OUTPUT) ? 0 : nv, ts, D);
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const f16x8 mh = lds_vec<f16x8>(&op.M[0][16 * t + l16][8 * grp]);
@@ -636,12 +664,12 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
             for (int j = 0; j < 8; ++j) vcur[j] = vnxt[j];
             __syncthreads();
         }
-        if (a.hT) {
+        if (hTp) {
 #pragma unroll
             for (int m = 0; m < 8; ++m)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    a.hT[sbase + (uint32_t)(16 * m + 4 * grp + j) * D + vc] = S[m][j];
+                    hTp[sbase + (uint32_t)(16 * m + 4 * grp + j) * D + vc] = S[m][j];
         }
     } else {
         const int hw = wave - NS;

@@ -7,6 +7,21 @@
 namespace kda {
 
 // Arguments of the fused forward kernel. Layouts are those of include/kda.h.
+// One slice of every chain of a fixed-length batch: tokens [t_begin, t_end)
+// of each row, from its own initial state into its own final state.
+enum : int {
+    TASK_IDENTITY_H0 = 1,   // start from the identity (the state is then the slice's transition map)
+    TASK_ZERO_V = 2,        // v read as zero
+    TASK_NO_OUTPUT = 4,     // o not written
+};
+struct FwdTask {
+    int t_begin, t_end;
+    const float* h0;        // [N, H, K, V] or nullptr (zero), unless TASK_IDENTITY_H0
+    float* hT;              // [N, H, K, V] or nullptr
+    int flags;
+};
+constexpr int kMaxTasks = 3;
+
 struct FwdArgs {
     const void* q;
     const void* k;
@@ -20,7 +35,17 @@ struct FwdArgs {
     int B, T, H, N;
     int nchains;         // N * H
     int scalar_gate;     // 1: one gate per (token, head) (Gated DeltaNet)
+    // ntasks > 0 (fixed-length batches only): chain c runs task c / (N * H) on
+    // (sequence, head) c % (N * H); nchains = ntasks * N * H, and h0/hT above
+    // are unused.
+    int ntasks;
+    FwdTask task[kMaxTasks];
 };
+
+// S_out = Pmap S_in + R per (sequence, head): the state at the end of a slice
+// from its transition map Pmap (K x K) and its zero-start end state R (K x V).
+hipError_t launch_affine_combine(const float* Pmap, const float* S_in, const float* R, float* S_out,
+                                 int nchains, hipStream_t stream);
 
 // One phase at a time (both input dtypes); used for fp32 inputs.
 int serial_workgroups(int nchains);

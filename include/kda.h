@@ -94,9 +94,19 @@ kda_status_t kda_fwd_check(const void* q, const void* k, const void* v, const fl
 /* The chunked KDA forward (prefill): o for every token and, when hT != NULL,
  * the final state of every (sequence, head). h0 == NULL starts from zero.
  * Runs as one fused kernel per (sequence, head, V-block) that reads every
- * input once; it needs no workspace. With T == 1 and no cu_seqlens (one
- * token per batch row) and 16-byte aligned o, h0, hT, it runs the decode
- * kernel of kda_decode_step instead. */
+ * input once. With T == 1 and no cu_seqlens (one token per batch row) and
+ * 16-byte aligned o, h0, hT, it runs the decode kernel of kda_decode_step
+ * instead.
+ * Few long chains (bf16, no cu_seqlens, T >= 12288, at most one chain per six
+ * compute units) are cut into three slices of whole 32-token chunks: the
+ * middle slice's state map is affine, S_end = Pmap S_start + R, so it is run
+ * from zero and from the identity alongside the first slice, and the later
+ * slices then run from their true start states (two passes of a third of the
+ * length each, plus one small product). That path needs 256 KiB per
+ * (sequence, head) of device memory: desc->workspace when it is at least that
+ * large, else a stream-ordered allocation on `stream`, freed on the same
+ * stream (if that allocation fails, the chains run whole). Every other case
+ * needs no workspace. */
 kda_status_t kda_fwd(const void* q, const void* k, const void* v, const float* g,
                      const float* beta, const int32_t* cu_seqlens, const float* h0,
                      void* o, float* hT, const kda_desc_t* desc, void* stream);
