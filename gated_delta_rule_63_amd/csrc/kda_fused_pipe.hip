@@ -428,7 +428,8 @@ template <int NS, bool SG>
 __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
     constexpr int NT = Split<NS>::NT, VB = Split<NS>::VB, P = Split<NS>::P;
     __shared__ Smem sm;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave: scalar branches on roles
     const int l16 = lane & 15, grp = lane >> 4;
     const bool is_state = wave < NS;
 
