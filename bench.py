@@ -28,7 +28,9 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 BYTES_PER_TOKEN_HEAD = 3 * 256 + 512 + 4 + 512   # q, k, v bf16 + g fp32 + beta + o fp32
 STATE_BYTES = 128 * 128 * 4                        # one (sequence, head) state, fp32
-FLOPS_PER_TOKEN_HEAD = 141013                      # chunked form at C = 64, see the design doc
+# Chunked form at C = 64: 2*(3KV + K(C-1)/2 + (C+1)/2*(2K+2V) + C^2/6) flop per
+# token-head with K = V = 128 (inter-chunk products, intra-chunk triangles, solve).
+FLOPS_PER_TOKEN_HEAD = 141013
 
 # Algorithmic bytes of each stage of the staged path (fp32 intermediates,
 # 32-token chunks), per token-head: each tensor read or written once.
@@ -77,8 +79,8 @@ def bench_decode(args):
     import workloads as W
     import gated_delta_rule_63_amd as kda
 
-    N, H = args.decode, W.CONFIGS["c2"].H
-    cfg = W.variant("c2", B=N, T=1, H=H, h0=True, name=f"decode N={N}")
+    N, H = args.decode, W.CONFIGS["T8192_H96"].H
+    cfg = W.variant("T8192_H96", B=N, T=1, H=H, h0=True, name=f"decode N={N}")
     inp = W.make_inputs(cfg, args.seed)
     dev = torch.device("cuda:0")
     cvt = lambda x: torch.from_numpy(W.bf16_bits(x).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -165,7 +167,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--config", default="c2")
+    ap.add_argument("--config", default="T8192_H96")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--protocol-repeats", type=int, default=5,

@@ -25,7 +25,7 @@ def _gpu():
 
 
 def step_inputs(N, H, seed, dtype="bf16", h0=True):
-    cfg = W.variant("c2", B=N, T=1, H=H, h0=h0, name=f"decode N={N} H={H}")
+    cfg = W.variant("T8192_H96", B=N, T=1, H=H, h0=h0, name=f"decode N={N} H={H}")
     if dtype == "fp32":
         cfg = W.variant(cfg, dtype="fp32")
     return W.make_inputs(cfg, seed, dtype=dtype)
@@ -78,7 +78,7 @@ def test_prefill_then_decode_steps():
     import torch
     import gated_delta_rule_63_amd as kda
     P, S_ = 300, 8
-    cfg = W.variant("c2", B=3, T=P + S_, H=4, h0=True, name="prefill+decode")
+    cfg = W.variant("T8192_H96", B=3, T=P + S_, H=4, h0=True, name="prefill+decode")
     inp = W.make_inputs(cfg, 6)
     t = to_device(inp, "bf16")
     pre = {k: (v[:, :P].contiguous() if k in ("q", "k", "v", "g", "beta") else v) for k, v in t.items()}

@@ -65,7 +65,7 @@ CASES = [
 def test_gdn_matches_oracle(what, kw, dtype):
     kw = dict(kw)
     kw.setdefault("gate", "scalar")
-    cfg = W.variant("c2", name="gdn " + what, **kw)
+    cfg = W.variant("T8192_H96", name="gdn " + what, **kw)
     check(W.make_inputs(cfg, 5, dtype=dtype), dtype, what)
 
 
@@ -75,7 +75,7 @@ def test_gdn_equals_kda_with_repeated_gate(dtype):
     the KDA arithmetic unchanged: bitwise equal to kda_fwd with the gate repeated."""
     import torch
     import gated_delta_rule_63_amd as kda
-    cfg = W.variant("c3a", T=400, H=3, seq_lens=(100, 37, 0, 263), gate="scalar_mild", name="gdn=kda")
+    cfg = W.variant("varlen6_T8192_H96", T=400, H=3, seq_lens=(100, 37, 0, 263), gate="scalar_mild", name="gdn=kda")
     inp = W.make_inputs(cfg, 6, dtype=dtype)
     t = to_device(inp, dtype)
     gs = torch.from_numpy(inp.g_scalar()).to(t["q"].device)
@@ -87,14 +87,14 @@ def test_gdn_equals_kda_with_repeated_gate(dtype):
 
 def test_gdn_headline_shape_sampled_heads():
     """T = 8192, H = 96 with a scalar gate: all heads computed, four compared with the oracle."""
-    cfg = W.variant("c2", gate="scalar", name="gdn c2")
-    check(W.make_inputs(cfg, 0), "bf16", "c2 shape, heads 0,31,64,95", heads=[0, 31, 64, 95])
+    cfg = W.variant("T8192_H96", gate="scalar", name="gdn T8192_H96")
+    check(W.make_inputs(cfg, 0), "bf16", "T=8192 H=96, heads 0,31,64,95", heads=[0, 31, 64, 95])
 
 
 def test_gdn_rejects_channel_gate_shape():
     import torch
     import gated_delta_rule_63_amd as kda
-    cfg = W.variant("c2", T=40, H=2, name="gdn shape")
+    cfg = W.variant("T8192_H96", T=40, H=2, name="gdn shape")
     t = to_device(W.make_inputs(cfg, 1), "bf16")
     with pytest.raises(ValueError):
         kda.gdn_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"])

@@ -30,7 +30,7 @@ def fwd(t, **kw):
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_run_to_run_bitwise(dtype):
-    cfg = W.variant("c3a", T=2000, H=4, seq_lens=(700, 1, 299, 1000), name="det")
+    cfg = W.variant("varlen6_T8192_H96", T=2000, H=4, seq_lens=(700, 1, 299, 1000), name="det")
     t = to_device(W.make_inputs(cfg, 1, dtype=dtype), dtype)
     o1, h1 = fwd(t)
     o2, h2 = fwd(t)
@@ -39,7 +39,7 @@ def test_run_to_run_bitwise(dtype):
 
 def test_h0_hT_alias():
     import torch
-    cfg = W.variant("c2", T=500, H=3, h0=True, gate="mild", name="alias")
+    cfg = W.variant("T8192_H96", T=500, H=3, h0=True, gate="mild", name="alias")
     t = to_device(W.make_inputs(cfg, 2), "bf16")
     o_ref, h_ref = fwd(t)
     state = t["h0"].clone()
@@ -52,7 +52,7 @@ def test_h0_hT_alias():
 def test_varlen_equals_per_sequence_runs():
     import torch
     lens = (65, 0, 1, 32, 33, 300)
-    cfg = W.variant("c3a", T=sum(lens), H=3, seq_lens=lens, name="split")
+    cfg = W.variant("varlen6_T8192_H96", T=sum(lens), H=3, seq_lens=lens, name="split")
     inp = W.make_inputs(cfg, 3)
     t = to_device(inp, "bf16")
     o, h = fwd(t)
@@ -79,7 +79,7 @@ def test_varlen_equals_per_sequence_runs():
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_handoff_at_chunk_boundary_is_bitwise(dtype):
     """Two halves with hT handed over as h0 equal one run when the split is a multiple of 32."""
-    cfg = W.variant("c2", T=2048, H=3, h0=True, gate="mild", name="handoff")
+    cfg = W.variant("T8192_H96", T=2048, H=3, h0=True, gate="mild", name="handoff")
     t = to_device(W.make_inputs(cfg, 4, dtype=dtype), dtype)
     o, h = fwd(t)
     m = 1024
@@ -94,7 +94,7 @@ def test_handoff_at_chunk_boundary_is_bitwise(dtype):
 def test_many_short_sequences():
     rng = np.random.default_rng(5)
     lens = tuple(int(x) for x in rng.integers(1, 10, size=1000))
-    cfg = W.variant("c3a", T=sum(lens), H=2, seq_lens=lens, name="1000 short sequences")
+    cfg = W.variant("varlen6_T8192_H96", T=sum(lens), H=2, seq_lens=lens, name="1000 short sequences")
     inp = W.make_inputs(cfg, 5)
     o, h = run_gpu(inp)
     ro, rs = run_oracle(inp)
@@ -105,7 +105,7 @@ def test_many_short_sequences():
 
 def test_linear_in_q():
     import torch
-    cfg = W.variant("c2", T=700, H=2, h0=True, name="lin")
+    cfg = W.variant("T8192_H96", T=700, H=2, h0=True, name="lin")
     t = to_device(W.make_inputs(cfg, 6), "bf16")
     o1, _ = fwd(t)
     t2 = dict(t, q=(t["q"].float() * 2.0).to(torch.bfloat16))   # exact in bf16
@@ -119,8 +119,8 @@ def test_c4_handoff_and_oracle():
     """T = 131072, H = 32 as one run and as 2 x 65536 with the state handed over;
     the halves must reproduce the single run, and sampled heads match the oracle."""
     import torch
-    log("[inv] c4: generating inputs")
-    inp = W.make_inputs(W.CONFIGS["c4"], 0)
+    log("[inv] T131072_H32: generating inputs")
+    inp = W.make_inputs(W.CONFIGS["T131072_H32"], 0)
     t = to_device(inp, "bf16")
     o, h = fwd(t)
     m = 65536
@@ -134,7 +134,7 @@ def test_c4_handoff_and_oracle():
     ro, rs = run_oracle(inp, heads)
     eo = rel_err(o.cpu().numpy()[:, :, heads], ro)
     es = rel_err(h.cpu().numpy()[:, heads], rs)
-    log(f"[inv] c4 heads {heads}: err_o {eo:.2e} err_hT {es:.2e}")
+    log(f"[inv] T131072_H32 heads {heads}: err_o {eo:.2e} err_hT {es:.2e}")
     assert eo <= TOL["bf16"][0] and es <= TOL["bf16"][1]
 
 
@@ -144,7 +144,7 @@ def test_split_over_workgroups_is_bitwise():
     (two-way split) equal the same heads run as a 20-head (eight-way) and a
     40-head (four-way) problem."""
     import torch
-    cfg = W.variant("c2", T=300, H=80, h0=True, gate="mild", name="split-ways")
+    cfg = W.variant("T8192_H96", T=300, H=80, h0=True, gate="mild", name="split-ways")
     t = to_device(W.make_inputs(cfg, 8), "bf16")
     o80, h80 = fwd(t)
     for H in (20, 40):

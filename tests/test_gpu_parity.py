@@ -25,21 +25,21 @@ def _gpu():
 # ---------------------------------------------------------------- small configs spanning tiles
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_c0_fp32(seed):
-    check(W.make_inputs(W.CONFIGS["c0"], seed), what=f"c0 seed {seed}")
+    check(W.make_inputs(W.CONFIGS["tiny_fp32"], seed), what=f"tiny fp32 seed {seed}")
 
 
 SMALL = [
-    W.variant("c2", T=1000, H=4, name="fixed T=1000 (ragged)"),
-    W.variant("c2", B=2, T=333, H=3, name="batch 2 T=333"),
-    W.variant("c2", T=1000, H=4, h0=True, name="T=1000 with h0"),
-    W.variant("c2", T=777, H=3, h0=True, gate="mild", name="mild decay with h0"),
-    W.variant("c2", T=512, H=2, gate="zero", name="g = 0 (plain delta rule)"),
-    W.variant("c2", T=300, H=2, h0=True, gate="mild", beta="zero", name="beta = 0 (pure decay)"),
-    W.variant("c2", T=300, H=2, keys="onehot", h0=True, gate="mild", name="one-hot keys"),
-    W.variant("c2", T=200, H=2, keys="same", name="identical keys"),
-    W.variant("c2", T=1 + 31 + 32 + 33 + 0 + 100 + 5, H=3, seq_lens=(1, 31, 32, 33, 0, 100, 5), h0=True,
+    W.variant("T8192_H96", T=1000, H=4, name="fixed T=1000 (ragged)"),
+    W.variant("T8192_H96", B=2, T=333, H=3, name="batch 2 T=333"),
+    W.variant("T8192_H96", T=1000, H=4, h0=True, name="T=1000 with h0"),
+    W.variant("T8192_H96", T=777, H=3, h0=True, gate="mild", name="mild decay with h0"),
+    W.variant("T8192_H96", T=512, H=2, gate="zero", name="g = 0 (plain delta rule)"),
+    W.variant("T8192_H96", T=300, H=2, h0=True, gate="mild", beta="zero", name="beta = 0 (pure decay)"),
+    W.variant("T8192_H96", T=300, H=2, keys="onehot", h0=True, gate="mild", name="one-hot keys"),
+    W.variant("T8192_H96", T=200, H=2, keys="same", name="identical keys"),
+    W.variant("T8192_H96", T=1 + 31 + 32 + 33 + 0 + 100 + 5, H=3, seq_lens=(1, 31, 32, 33, 0, 100, 5), h0=True,
               name="varlen edge lengths"),
-    W.variant("c2", T=1, H=2, h0=True, name="single token"),
+    W.variant("T8192_H96", T=1, H=2, h0=True, name="single token"),
 ]
 
 
@@ -52,7 +52,7 @@ def test_small(cfg, dtype):
 def test_empty_sequences_keep_state():
     import torch
     import gated_delta_rule_63_amd as kda
-    cfg = W.variant("c2", T=40, H=2, seq_lens=(0, 40, 0), h0=True, name="zero-length")
+    cfg = W.variant("T8192_H96", T=40, H=2, seq_lens=(0, 40, 0), h0=True, name="zero-length")
     inp = W.make_inputs(cfg, 3)
     o, hT = run_gpu(inp)
     ro, rs = run_oracle(inp)
@@ -60,7 +60,7 @@ def test_empty_sequences_keep_state():
     np.testing.assert_array_equal(hT[2], inp.h0[2])
     assert rel_err(o, ro) <= 2e-2 and rel_err(hT, rs) <= 1e-2
     # T = 0: nothing to compute, hT = h0
-    t = to_device(W.make_inputs(W.variant("c2", T=8, H=2, h0=True), 0), "bf16")
+    t = to_device(W.make_inputs(W.variant("T8192_H96", T=8, H=2, h0=True), 0), "bf16")
     z = {k: (v[:, :0].contiguous() if k in ("q", "k", "v", "g", "beta") else v) for k, v in t.items()}
     o0, h = kda.fwd(z["q"], z["k"], z["v"], z["g"], z["beta"], initial_state=z["h0"])
     torch.cuda.synchronize()
@@ -93,7 +93,7 @@ def test_worked_example_embedded():
 
 
 # ---------------------------------------------------------------- full-size workloads
-@pytest.mark.parametrize("name", ["c1", "c2", "c3a", "c3b"])
+@pytest.mark.parametrize("name", ["T8192_H64", "T8192_H96", "varlen6_T8192_H96", "varlen8x1024_H96"])
 def test_full_config(name):
     log(f"[full] {name}: generating inputs")
     check(W.make_inputs(W.CONFIGS[name], 0), what=f"{name} full")
@@ -101,6 +101,6 @@ def test_full_config(name):
 
 def test_c4_sampled_heads():
     """T = 131072, H = 32: every output is computed, four heads are compared with the oracle."""
-    log("[full] c4: generating inputs")
-    inp = W.make_inputs(W.CONFIGS["c4"], 0)
-    check(inp, heads=[0, 9, 22, 31], what="c4 heads 0,9,22,31")
+    log("[full] T131072_H32: generating inputs")
+    inp = W.make_inputs(W.CONFIGS["T131072_H32"], 0)
+    check(inp, heads=[0, 9, 22, 31], what="T131072_H32 heads 0,9,22,31")

@@ -33,7 +33,7 @@ def fwd(t, final_state=None, gdn=None):
 # so the slices' start states matter everywhere; "mild" spans about 120 tokens.
 @pytest.mark.parametrize("gate,h0", [("zero", True), ("mild", True), ("bj", False)])
 def test_sliced_chain_matches_oracle(gate, h0):
-    cfg = W.variant("c4", T=12320, H=4, gate=gate, h0=h0, name=f"slices {gate}")
+    cfg = W.variant("T131072_H32", T=12320, H=4, gate=gate, h0=h0, name=f"slices {gate}")
     inp = W.make_inputs(cfg, 11)
     t = to_device(inp, "bf16")
     o, hT = fwd(t)
@@ -48,7 +48,7 @@ def test_sliced_chain_state_alias():
     """h0 == hT (in place) through the sliced path: the first pass reads h0 before
     the last one writes hT."""
     import torch
-    cfg = W.variant("c4", T=12288, H=2, gate="zero", h0=True, name="slices alias")
+    cfg = W.variant("T131072_H32", T=12288, H=2, gate="zero", h0=True, name="slices alias")
     inp = W.make_inputs(cfg, 12)
     t = to_device(inp, "bf16")
     o_ref, h_ref = fwd(t)
@@ -61,7 +61,7 @@ def test_sliced_chain_state_alias():
 def test_sliced_chain_scalar_gate():
     import torch
     import oracle
-    cfg = W.variant("c4", T=12288, H=3, gate="scalar_mild", h0=True, name="slices gdn")
+    cfg = W.variant("T131072_H32", T=12288, H=3, gate="scalar_mild", h0=True, name="slices gdn")
     inp = W.make_inputs(cfg, 13)
     t = to_device(inp, "bf16")
     gs = torch.from_numpy(inp.g_scalar()).to(t["q"].device)

@@ -40,10 +40,10 @@ def close(got, ref, what, tol=STAGE_TOL):
 
 
 CASES = [
-    W.variant("c2", T=1 + 31 + 32 + 33 + 0 + 70 + 5, H=3, seq_lens=(1, 31, 32, 33, 0, 70, 5), h0=True,
+    W.variant("T8192_H96", T=1 + 31 + 32 + 33 + 0 + 70 + 5, H=3, seq_lens=(1, 31, 32, 33, 0, 70, 5), h0=True,
               gate="mild", name="varlen edge lengths, mild decay"),
-    W.variant("c2", B=2, T=100, H=2, name="batch 2 ragged"),
-    W.variant("c0", T=96, name="fp32 inputs", h0=True),
+    W.variant("T8192_H96", B=2, T=100, H=2, name="batch 2 ragged"),
+    W.variant("tiny_fp32", T=96, name="fp32 inputs", h0=True),
 ]
 
 
@@ -101,7 +101,7 @@ def test_stages_against_chunk_algebra(cfg):
     close(hT.cpu().numpy(), hT_ref, f"{cfg.name} hT vs chunk algebra", STAGE_TOL)
 
 
-@pytest.mark.parametrize("name", ["c0", "c2", "c3a"])
+@pytest.mark.parametrize("name", ["tiny_fp32", "T8192_H96", "varlen6_T8192_H96"])
 def test_staged_end_to_end(name):
     import torch
     import gated_delta_rule_63_amd as kda

@@ -349,7 +349,7 @@ def test_chunk_intermediates():
 
 def test_gate_range_of_workloads():
     """Gate values stay in [-5, 0] (the documented input range) and beta in (0, 1)."""
-    inp = W.make_inputs(W.CONFIGS["c0"], 0)
+    inp = W.make_inputs(W.CONFIGS["tiny_fp32"], 0)
     assert inp.g.min() >= -5.0 and inp.g.max() <= 0.0
     assert inp.beta.min() > 0.0 and inp.beta.max() < 1.0
 
@@ -358,7 +358,7 @@ def test_workloads_match_pages_table():
     """The varlen mixes and shapes match the H20 table (tests/golden/h20_workloads.json)."""
     tab = json.load(open(os.path.join(GOLDEN, "h20_workloads.json")))
     rows = {(r["H"], tuple(r["seq_lens"]) if r["seq_lens"] else None) for r in tab["rows"]}
-    for name in ["c1", "c2", "c3a", "c3b"]:
+    for name in ["T8192_H64", "T8192_H96", "varlen6_T8192_H96", "varlen8x1024_H96"]:
         c = W.CONFIGS[name]
         assert c.T == 8192 and (c.H, c.seq_lens) in rows, name
     assert tab["protocol"] == {"warmup": 30, "iters": 200, "repeats": 5}
@@ -428,10 +428,10 @@ def test_gdn_rotation_invariance():
 
 
 def test_scalar_gate_workload():
-    cfg = W.variant("c2", T=64, H=2, gate="scalar", name="gdn")
+    cfg = W.variant("T8192_H96", T=64, H=2, gate="scalar", name="gdn")
     inp = W.make_inputs(cfg, 0)
     gs = inp.g_scalar()
     assert gs.shape == (1, 64, 2) and np.all(gs <= 0) and np.all(gs >= -5)
-    base = W.make_inputs(W.variant("c2", T=64, H=2, name="kda"), 0)
+    base = W.make_inputs(W.variant("T8192_H96", T=64, H=2, name="kda"), 0)
     assert np.array_equal(base.q, inp.q) and np.array_equal(base.beta, inp.beta)
     assert np.array_equal(gs, base.g[..., 0])    # channel 0 of the same draw

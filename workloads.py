@@ -77,15 +77,16 @@ class Config:
         return self.B * self.T * self.H
 
 
-# The five workloads. "c2" is the headline (T=8192, H=96).
+# The workloads: the pages' benchmark shapes (the headline is T=8192, H=96) and a
+# tiny fp32 case.
 VARLEN_MIX = (1300, 547, 2048, 963, 271, 3063)
 CONFIGS = {
-    "c0": Config("c0", 1, 256, 2, dtype="fp32", note="tiny fixed, fp32 inputs, h0 = 0"),
-    "c1": Config("c1", 1, 8192, 64, note="fixed-length prefill, H=64"),
-    "c2": Config("c2", 1, 8192, 96, note="fixed-length prefill, H=96 (headline)"),
-    "c3a": Config("c3a", 1, 8192, 96, seq_lens=VARLEN_MIX, h0=True, note="varlen 6-sequence mix"),
-    "c3b": Config("c3b", 1, 8192, 96, seq_lens=(1024,) * 8, h0=True, note="varlen 8 x 1024"),
-    "c4": Config("c4", 1, 131072, 32, h0=True, note="long-context stateful prefill"),
+    "tiny_fp32": Config("tiny_fp32", 1, 256, 2, dtype="fp32", note="tiny fixed, fp32 inputs, h0 = 0"),
+    "T8192_H64": Config("T8192_H64", 1, 8192, 64, note="fixed-length prefill, H=64"),
+    "T8192_H96": Config("T8192_H96", 1, 8192, 96, note="fixed-length prefill, H=96 (headline)"),
+    "varlen6_T8192_H96": Config("varlen6_T8192_H96", 1, 8192, 96, seq_lens=VARLEN_MIX, h0=True, note="varlen 6-sequence mix"),
+    "varlen8x1024_H96": Config("varlen8x1024_H96", 1, 8192, 96, seq_lens=(1024,) * 8, h0=True, note="varlen 8 x 1024"),
+    "T131072_H32": Config("T131072_H32", 1, 131072, 32, h0=True, note="long-context stateful prefill"),
 }
 
 
