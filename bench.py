@@ -174,6 +174,9 @@ def main():
                     help="extra repeats of --steps iterations (the pages' 30/200/5 protocol)")
     ap.add_argument("--path", choices=["fused", "staged"], default="fused",
                     help="fused: kda_fwd (the hot path); staged: kda_fwd_staged (five kernels)")
+    ap.add_argument("--kernel", choices=["auto", "pipe", "serial", "chunk16"], default="auto",
+                    help="fused path: run this one forward kernel (kda_fwd_kernel); chunk16 is the "
+                         "16-token-chunk ablation of the serial kernel")
     ap.add_argument("--stages", action="store_true", help="also time each staged-path kernel on its own")
     ap.add_argument("--decode", type=int, default=0, metavar="N",
                     help="time the in-place decode step for N sequences (H = 96) instead of the prefill")
@@ -217,7 +220,7 @@ def main():
 
     if args.path == "fused":
         def step():
-            kda.fwd(q, k, v, g, beta, cu_seqlens=cu, initial_state=h0, out=o, final_state=hT)
+            kda.fwd(q, k, v, g, beta, cu_seqlens=cu, initial_state=h0, out=o, final_state=hT, kernel=args.kernel)
     else:
         st = kda.Staged(q, k, v, g, beta, cu_seqlens=cu, initial_state=h0)
 
@@ -296,7 +299,14 @@ def main():
     bytes_ = alg_bytes(cfg)
     achieved = bytes_ / (ms / 1e3) / 1e9
     flops = cfg.token_heads * FLOPS_PER_TOKEN_HEAD
-    traffic = traffic_from_profile(cfg.name)
+    if args.path == "staged":
+        kname = "staged path (5 kernels)"
+    elif args.kernel == "auto":
+        kname = "kda_fwd_pipe" if cfg.dtype == "bf16" else "kda_fwd_fused (serial)"
+    else:
+        kname = {"pipe": "kda_fwd_pipe", "serial": "kda_fwd_fused (serial)", "chunk16": "kda_fwd_chunk16"}[args.kernel]
+    # the counter summary covers the pipelined kernel as kda_fwd runs it
+    traffic = traffic_from_profile(cfg.name) if (kname == "kda_fwd_pipe" and args.kernel == "auto") else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -317,13 +327,11 @@ def main():
         "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": cfg.dtype, "data": "synthetic",
-        "config": {"workload": desc, "global_batch": cfg.B, "seq_len": cfg.T, "heads": cfg.H,
-                   "parallelism": "single GPU"},
+        "config": {"workload": desc + ("" if args.kernel == "auto" else f", kernel {args.kernel}"),
+                   "global_batch": cfg.B, "seq_len": cfg.T, "heads": cfg.H, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "kda_fwd_pipe" if (args.path == "fused" and cfg.dtype == "bf16")
-                     else ("kda_fwd_fused (serial)" if args.path == "fused" else "staged path (5 kernels)"),
-                     "alg_bytes_per_launch": bytes_},
+                     "kernel": kname, "alg_bytes_per_launch": bytes_},
         "mfma": {"achieved": flops / (ms / 1e3) / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": flops / (ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
         "protocol": {"repeats": len(reps), "iters": args.steps, "median_ms": float(np.median(reps)) if reps else None,

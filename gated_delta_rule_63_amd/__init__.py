@@ -14,7 +14,7 @@ from typing import Optional, Tuple
 
 import torch
 
-from ._lib import KDA_BF16, KDA_F32, Desc, KDAError, Layout, lib, status_string  # noqa: F401
+from ._lib import KDA_BF16, KDA_F32, KERNELS, Desc, KDAError, Layout, lib, status_string  # noqa: F401
 
 __all__ = ["fwd", "gdn_fwd", "decode_step", "fwd_staged", "Staged", "KDAError", "status_string", "version"]
 
@@ -58,15 +58,23 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
         cu_seqlens: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
         output_final_state: bool = True, out: Optional[torch.Tensor] = None,
         final_state: Optional[torch.Tensor] = None,
-        stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+        stream: Optional[torch.cuda.Stream] = None,
+        kernel: str = "auto") -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """KDA chunked forward. Shapes: q, k, v, g [B, T, H, 128]; beta [B, T, H];
     cu_seqlens int32 [N + 1] (B == 1); initial_state / final state [N, H, 128, 128] fp32.
 
     Returns (o fp32 [B, T, H, 128], hT or None). Tensors must be contiguous and on
     one GPU; q, k, v share a dtype (bf16 or fp32); g and beta are fp32.
+    kernel: "auto" (kda_fwd), or "pipe", "serial", "chunk16" to run that one
+    forward kernel (kda_fwd_kernel).
     """
-    return _forward("kda_fwd", q, k, v, g, beta, cu_seqlens, initial_state, output_final_state,
-                    out, final_state, stream)
+    if kernel == "auto":
+        return _forward("kda_fwd", q, k, v, g, beta, cu_seqlens, initial_state, output_final_state,
+                        out, final_state, stream)
+    if kernel not in KERNELS:
+        raise ValueError(f"kernel must be one of {sorted(KERNELS)}")
+    return _forward("kda_fwd_kernel", q, k, v, g, beta, cu_seqlens, initial_state, output_final_state,
+                    out, final_state, stream, KERNELS[kernel])
 
 
 def gdn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
@@ -81,7 +89,7 @@ def gdn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, 
 
 
 def _forward(entry, q, k, v, g, beta, cu_seqlens, initial_state, output_final_state, out, final_state,
-             stream):
+             stream, *extra):
     _check_inputs(q, k, v, g, beta, cu_seqlens, scalar_gate=(entry == "kda_gdn_fwd"))
     d = _desc(q, cu_seqlens)
     B, T, H, _ = q.shape
@@ -96,7 +104,8 @@ def _forward(entry, q, k, v, g, beta, cu_seqlens, initial_state, output_final_st
             (d.num_seqs, H, D, D), dtype=torch.float32, device=q.device)
     s = (stream or torch.cuda.current_stream(q.device)).cuda_stream
     rc = getattr(lib(), entry)(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
-                               _ptr(initial_state), _ptr(o), _ptr(hT), ctypes.byref(d), ctypes.c_void_p(s))
+                               _ptr(initial_state), _ptr(o), _ptr(hT), ctypes.byref(d), *extra,
+                               ctypes.c_void_p(s))
     if rc != 0:
         raise KDAError(rc, entry)
     return o, hT

@@ -271,6 +271,25 @@ kda_status_t kda_gdn_fwd(const void* q, const void* k, const void* v, const floa
     return run_fwd(a, desc, o, h0, hT, cu_seqlens != nullptr, stream);
 }
 
+kda_status_t kda_fwd_kernel(const void* q, const void* k, const void* v, const float* g,
+                            const float* beta, const int32_t* cu_seqlens, const float* h0, void* o,
+                            float* hT, const kda_desc_t* desc, int32_t kernel, void* stream) {
+    const kda_status_t st = check(q, k, v, g, beta, cu_seqlens, o, desc);
+    if (st != KDA_OK) return st;
+    const bool f32 = desc->in_dtype == KDA_F32;
+    if (kernel < KDA_KERNEL_AUTO || kernel > KDA_KERNEL_CHUNK16) return KDA_ERR_UNSUPPORTED;
+    if (f32 && (kernel == KDA_KERNEL_PIPE || kernel == KDA_KERNEL_CHUNK16)) return KDA_ERR_UNSUPPORTED;
+    const kda::FwdArgs a = fwd_args(q, k, v, g, beta, cu_seqlens, h0, o, hT, desc);
+    if (kernel == KDA_KERNEL_AUTO) return run_fwd(a, desc, o, h0, hT, cu_seqlens != nullptr, stream);
+    if (a.nchains == 0) return KDA_OK;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (kernel == KDA_KERNEL_PIPE) e = kda::launch_fwd_pipe(a, device_cus(), s);
+    else if (kernel == KDA_KERNEL_SERIAL) e = kda::launch_fwd_serial(a, f32, s);
+    else e = kda::launch_fwd_chunk16(a, s);
+    return hip_status(e);
+}
+
 kda_status_t kda_decode_step(const void* q, const void* k, const void* v, const float* g,
                              const float* beta, const float* state_in, void* o, float* state_out,
                              const kda_desc_t* desc, void* stream) {

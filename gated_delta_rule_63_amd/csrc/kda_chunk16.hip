@@ -1,0 +1,370 @@
+// kda_chunk16.hip -- the fused chunked KDA forward with 16-token chunks (bf16 inputs).
+//
+// The same four steps per chunk as the one-phase-at-a-time kernel
+// (kda_fused_serial.hip), with the same workgroup shape (4 waves of 16 V
+// columns) and the same operand precisions, but chunks of C = 16 tokens
+// instead of 32. A chunk is then one 16 x 16 block: A and M are one tile each,
+// (I + A)^{-1} is one forward substitution and there is no off-diagonal block
+// to substitute. FlashKDA's v1 chose this chunk length for the bf16 range, a
+// cheap 16 x 16 inverse and portability (toolarium.ru page, section "Где
+// ограничения прямо сейчас"); this kernel exists to measure that choice on
+// gfx950 against the 32-token kernels, through kda_fwd_kernel.
+//
+// Per chunk, with Gamma the in-chunk cumulative log gate and ref = Gamma at
+// token 7 (so every factor lies in [e^-40, e^40] for g >= -5):
+//   A     = tril_-1( Diag(beta) (K e^{Gamma - ref}) (K e^{ref - Gamma})^T ),  T = (I + A)^{-1}
+//   Delta = T Diag(beta) (V - (K e^{Gamma}) S)
+//   O     = (Q e^{Gamma}) S + tril_0( (Q e^{Gamma - ref}) (K e^{ref - Gamma})^T ) Delta
+//   S    <- Diag(e^{Gamma_last}) S + (K e^{Gamma_last - Gamma})^T Delta
+// (the chunked form of the delta rule with channel-wise decay; donniechu.com
+// page, section on the KDA recurrence, and toolarium.ru page, section "Почему
+// это новость про инфраструктуру").
+//
+// Products over the 16 tokens (T Delta, M Delta, Kt^T Delta) run on
+// v_mfma_f32_16x16x16_f16, whose B operand (lane l: K-slots 4*(l/16) + j of
+// column l % 16) is the accumulator layout of a 16 x 16 result (rows
+// 4*(l/16) + j of column l % 16): Delta feeds the next product from registers.
+// Products over the 128 channels use 16x16x32 MFMAs with the channel order of
+// kperm(), as in the 32-token kernels.
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+namespace c16 {
+
+constexpr int C = 16;          // chunk length
+constexpr int NW = 4;          // waves per workgroup, each owns 16 V columns
+constexpr int NT = 64 * NW;    // threads per workgroup
+constexpr int VB = 16 * NW;    // V columns per workgroup
+constexpr int P = D / VB;      // workgroups per (sequence, head)
+constexpr int LDP = D + 8;     // padded row of a 2-byte [row][128] array
+constexpr int LDT = C + 4;     // padded row of a 2-byte [row][16] array (8-byte aligned rows)
+constexpr int LDA = C + 4;     // padded row of the fp32 A tile
+constexpr int LDV = VB + 4;    // padded row of the staged V tile
+constexpr float LOG2E = 1.4426950408889634f;
+static_assert(NT == 4 * (D / 2), "the scan maps one thread to each (channel pair, 4-token quarter)");
+static_assert(NT * 4 == C * VB, "one 4-element slice of the V tile per thread");
+
+struct alignas(16) Smem {
+    __bf16 Ka[2][C][LDP];       // k e^{Gamma_r - ref}, [hi, lo]: row factor of A
+    __bf16 Qa[2][C][LDP];       // q e^{Gamma_r - ref}, [hi, lo]: row factor of M
+    __bf16 Kb[2][C][LDP];       // k e^{ref - Gamma_r}, [hi, lo]: column factor of A and M
+    _Float16 Kg[C][LDP];        // k e^{Gamma_r}, channels in kperm order within 32-groups
+    _Float16 Qg[C][LDP];        // q e^{Gamma_r}, same order
+    _Float16 KtT[2][D][LDT];    // (k e^{Gamma_last - Gamma_r})^T, [hi, lo][channel][token]
+    float Ad[C][LDA];           // beta-scaled strictly lower A
+    _Float16 Tm[C][LDT];        // (I + A)^{-1}, [row][col]
+    _Float16 M[2][C][LDT];      // lower gated Q K^T, [hi, lo][row][col]
+    float V[C][LDV];            // this workgroup's V columns of the chunk
+    float gl[D];                // e^{Gamma_last}: the chunk's decay per channel
+    float beta[C];
+    float qtot[4][D];           // sum of g log2(e) over each 4-token quarter
+};
+
+// One thread's inputs of a chunk: channels 2cp, 2cp+1 of tokens 4qq .. 4qq+3,
+// four V elements and one beta.
+struct Fetch {
+    float2 g[4];
+    uint32_t k[4], q[4];   // two bf16 each
+    uint2 v;               // four bf16 of the V tile
+    float beta;
+};
+
+struct Offs {
+    uint32_t gk;   // (4qq) * ts + 2cp: q, k, g of token 4qq, channels 2cp, 2cp+1
+    uint32_t v;    // (tid >> 4) * ts + vcol0 + (tid & 15) * 4: V tile slice
+};
+
+__device__ __forceinline__ float2 bf2(uint32_t u) {
+    return make_float2(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
+}
+
+__device__ __forceinline__ f32x4 mfma16k(const f16x4& a, const f16x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+// Tokens at or past nv read as zero, which makes them vanish from every product.
+__device__ __forceinline__ void fetch(Fetch& f, const FwdArgs& a, long long cbase, long long cbeta,
+                                      uint32_t ts, const Offs& of, int nv, int qq, int tid) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int rr = 4 * qq + t;
+        const uint32_t o = of.gk + (uint32_t)t * ts;
+        if (rr < nv) {
+            f.g[t] = *reinterpret_cast<const float2*>(a.g + cbase + o);
+            f.k[t] = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.k) + cbase + o);
+            f.q[t] = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.q) + cbase + o);
+        } else {
+            f.g[t] = make_float2(0.f, 0.f);
+            f.k[t] = 0u;
+            f.q[t] = 0u;
+        }
+    }
+    f.beta = (tid < nv) ? a.beta[cbeta + (uint32_t)tid * (uint32_t)a.H] : 0.f;
+    f.v = ((tid >> 4) < nv) ? *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.v) + cbase + of.v)
+                            : make_uint2(0u, 0u);
+}
+
+// Forward substitution of the unit-lower-triangular 16 x 16 matrix I + A:
+// lane j (of 16) returns column j of (I + A)^{-1}.
+__device__ __forceinline__ void unit_lower_inverse(const float (*A)[LDA], int j, float x[16]) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        float s = (r == j) ? 1.f : 0.f;
+#pragma unroll
+        for (int i = 0; i < r; ++i) s = fmaf(-A[r][i], x[i], s);
+        x[r] = s;
+    }
+}
+
+__global__ __launch_bounds__(NT, 1) void kda_fwd_chunk16(FwdArgs a) {
+    __shared__ Smem sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, grp = lane >> 4;
+
+    // Workgroup -> chain: the P V-blocks of one (sequence, head) take ids
+    // congruent mod 8, so they run on one XCD and share its L2.
+    const int bid = blockIdx.x;
+    const int xcd = bid & 7, rest = bid >> 3;
+    const int vblk = rest % P;
+    const int chain = (rest / P) * 8 + xcd;
+    if (chain >= a.nchains) return;
+    const int n = chain / a.H, h = chain % a.H;
+    int row, t0, t1;
+    if (a.cu) { row = 0; t0 = a.cu[n]; t1 = a.cu[n + 1]; }
+    else      { row = n; t0 = 0;       t1 = a.T; }
+    const uint32_t ts = (uint32_t)a.H * D;                          // elements per token
+    const long long base = (long long)row * a.T * ts + (long long)h * D;
+    const long long bbase = (long long)row * a.T * a.H + h;         // beta of (row, t = 0, h)
+    const int vcol0 = vblk * VB;
+    const int vc = vcol0 + wave * 16 + l16;                         // this lane's V column
+    const long long sbase = ((long long)n * a.H + h) * D * D;
+
+    f32x4 S[8];                                  // rows 16m + 4grp + j, column vc
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            S[m][j] = a.h0 ? a.h0[sbase + (uint32_t)(16 * m + 4 * grp + j) * D + vc] : 0.f;
+
+    const int cp = tid & 63, qq = tid >> 6;      // scan thread: channel pair, 4-token quarter
+    Offs of;
+    of.gk = (uint32_t)(4 * qq) * ts + 2 * cp;
+    of.v = (uint32_t)(tid >> 4) * ts + vcol0 + (tid & 15) * 4;
+    const uint32_t ooff = (uint32_t)(4 * grp) * ts + vc;           // o: (row 4grp, column vc)
+
+    Fetch f;
+    if (t0 < t1) fetch(f, a, base + (long long)t0 * ts, bbase + (long long)t0 * a.H, ts, of, min(C, t1 - t0), qq, tid);
+
+    for (int cs = t0; cs < t1; cs += C) {
+        const int nv = min(C, t1 - cs);
+
+        // ---- (1) gate scan (log2 units) over tokens 4qq .. 4qq+3, channels 2cp, 2cp+1
+        float L[2][4];
+        {
+            float r0 = 0.f, r1 = 0.f;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                r0 += f.g[t].x * LOG2E;
+                r1 += f.g[t].y * LOG2E;
+                L[0][t] = r0;
+                L[1][t] = r1;
+            }
+            *reinterpret_cast<float2*>(&sm.qtot[qq][2 * cp]) = make_float2(r0, r1);
+        }
+        if (tid < C) sm.beta[tid] = f.beta;
+        {
+            const float2 p0 = bf2(f.v.x), p1 = bf2(f.v.y);
+            *reinterpret_cast<float4*>(&sm.V[tid >> 4][(tid & 15) * 4]) = make_float4(p0.x, p0.y, p1.x, p1.y);
+        }
+        float kv[2][4], qv[2][4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const float2 kk2 = bf2(f.k[t]), qq2 = bf2(f.q[t]);
+            kv[0][t] = kk2.x; kv[1][t] = kk2.y; qv[0][t] = qq2.x; qv[1][t] = qq2.y;
+        }
+        __syncthreads();
+        // the registers are consumed: fetch the next chunk while this one computes
+        if (cs + C < t1)
+            fetch(f, a, base + (long long)(cs + C) * ts, bbase + (long long)(cs + C) * a.H, ts, of,
+                  min(C, t1 - cs - C), qq, tid);
+        {
+            float d[2][4], c1[2], c2[2];
+#pragma unroll
+            for (int ch = 0; ch < 2; ++ch) {
+                const int c = 2 * cp + ch;
+                const float qt0 = sm.qtot[0][c], qt1 = sm.qtot[1][c], qt2 = sm.qtot[2][c], qt3 = sm.qtot[3][c];
+                const float ref = qt0 + qt1;                   // Gamma at token 7
+                const float tot = ref + (qt2 + qt3);           // Gamma_last
+                const float off = qq == 0 ? 0.f : qq == 1 ? qt0 : qq == 2 ? ref : ref + qt2;
+                c1[ch] = exp2f(ref);                           // e^{ref}              -> K e^Gamma, Q e^Gamma
+                c2[ch] = exp2f(tot - ref);                     // e^{Gamma_last - ref} -> Kt
+                if (qq == 0) sm.gl[c] = exp2f(tot);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) d[ch][t] = L[ch][t] + off - ref;   // |d| <= 8 * 5 * log2(e)
+            }
+            const int cpos = ((2 * cp) & ~31) | kperm((2 * cp) & 31);   // channel pair position in Kg/Qg
+            float kt[2][4];                                              // [channel][token]
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                float ka[2], qa[2], kb[2];
+#pragma unroll
+                for (int ch = 0; ch < 2; ++ch) {
+                    const float e1 = exp2f(d[ch][t]), e2 = exp2f(-d[ch][t]);
+                    ka[ch] = kv[ch][t] * e1;
+                    qa[ch] = qv[ch][t] * e1;
+                    kb[ch] = kv[ch][t] * e2;
+                    kt[ch][t] = kb[ch] * c2[ch];
+                }
+                const int rr = 4 * qq + t;
+                uint32_t hi, lo;
+                split_bf16x2(ka[0], ka[1], hi, lo);
+                *reinterpret_cast<uint32_t*>(&sm.Ka[0][rr][2 * cp]) = hi;
+                *reinterpret_cast<uint32_t*>(&sm.Ka[1][rr][2 * cp]) = lo;
+                split_bf16x2(qa[0], qa[1], hi, lo);
+                *reinterpret_cast<uint32_t*>(&sm.Qa[0][rr][2 * cp]) = hi;
+                *reinterpret_cast<uint32_t*>(&sm.Qa[1][rr][2 * cp]) = lo;
+                split_bf16x2(kb[0], kb[1], hi, lo);
+                *reinterpret_cast<uint32_t*>(&sm.Kb[0][rr][2 * cp]) = hi;
+                *reinterpret_cast<uint32_t*>(&sm.Kb[1][rr][2 * cp]) = lo;
+                *reinterpret_cast<uint32_t*>(&sm.Kg[rr][cpos]) = pack_f16(ka[0] * c1[0], ka[1] * c1[1]);
+                *reinterpret_cast<uint32_t*>(&sm.Qg[rr][cpos]) = pack_f16(qa[0] * c1[0], qa[1] * c1[1]);
+            }
+            // Kt^T: the thread's four tokens are one 8-byte run of a channel's row
+#pragma unroll
+            for (int ch = 0; ch < 2; ++ch) {
+                uint32_t h01, l01, h23, l23;
+                split_f16x2(kt[ch][0], kt[ch][1], h01, l01);
+                split_f16x2(kt[ch][2], kt[ch][3], h23, l23);
+                *reinterpret_cast<uint2*>(&sm.KtT[0][2 * cp + ch][4 * qq]) = make_uint2(h01, h23);
+                *reinterpret_cast<uint2*>(&sm.KtT[1][2 * cp + ch][4 * qq]) = make_uint2(l01, l23);
+            }
+        }
+        __syncthreads();
+
+        // ---- (2) wave 0: A, then (I + A)^{-1}; wave 1: M
+        if (wave < 2) {
+            const bool isM = wave == 1;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk) {
+                const int off = 32 * kk + 8 * grp;
+                const bf16x8 rh = lds_vec<bf16x8>(isM ? &sm.Qa[0][l16][off] : &sm.Ka[0][l16][off]);
+                const bf16x8 rl = lds_vec<bf16x8>(isM ? &sm.Qa[1][l16][off] : &sm.Ka[1][l16][off]);
+                const bf16x8 ch = lds_vec<bf16x8>(&sm.Kb[0][l16][off]);
+                const bf16x8 cl = lds_vec<bf16x8>(&sm.Kb[1][l16][off]);
+                acc = mfma16(rh, ch, acc);
+                acc = mfma16(rh, cl, acc);
+                acc = mfma16(rl, ch, acc);
+            }
+            if (isM) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 4 * grp + j;
+                    split16((l16 <= r) ? acc[j] : 0.f, sm.M[0][r][l16], sm.M[1][r][l16]);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 4 * grp + j;
+                    sm.Ad[r][l16] = (l16 < r) ? sm.beta[r] * acc[j] : 0.f;
+                }
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                if (grp == 0) {
+                    float x[16];
+                    unit_lower_inverse(sm.Ad, l16, x);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) sm.Tm[r][l16] = (_Float16)x[r];
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- (3)+(4) state-side products for this wave's 16 columns
+        {
+            f16x8 SB[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    SB[kk][j] = (_Float16)S[2 * kk][j];
+                    SB[kk][4 + j] = (_Float16)S[2 * kk + 1][j];
+                }
+            f32x4 Pt = {0.f, 0.f, 0.f, 0.f}, Ot = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int off = 32 * kk + 8 * grp;
+                Pt = mfma16(lds_vec<f16x8>(&sm.Kg[l16][off]), SB[kk], Pt);
+                Ot = mfma16(lds_vec<f16x8>(&sm.Qg[l16][off]), SB[kk], Ot);
+            }
+            // Delta = T beta (V - P)
+            f16x4 Bh, Bl;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * grp + j;
+                const half2s u = split16(sm.beta[r] * (sm.V[r][wave * 16 + l16] - Pt[j]));
+                Bh[j] = u.hi;
+                Bl[j] = u.lo;
+            }
+            const f16x4 th = lds_vec<f16x4>(&sm.Tm[l16][4 * grp]);
+            f32x4 Dl = {0.f, 0.f, 0.f, 0.f};
+            Dl = mfma16k(th, Bh, Dl);
+            Dl = mfma16k(th, Bl, Dl);
+            f16x4 DBh, DBl;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const half2s u = split16(Dl[j]);
+                DBh[j] = u.hi;
+                DBl[j] = u.lo;
+            }
+            // O = (Q e^Gamma) S + M Delta
+            {
+                const f16x4 mh = lds_vec<f16x4>(&sm.M[0][l16][4 * grp]);
+                const f16x4 ml = lds_vec<f16x4>(&sm.M[1][l16][4 * grp]);
+                f32x4 acc = Ot;
+                acc = mfma16k(mh, DBh, acc);
+                acc = mfma16k(mh, DBl, acc);
+                acc = mfma16k(ml, DBh, acc);
+                float* och = a.o + base + (long long)cs * ts;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (4 * grp + j < nv) och[ooff + (uint32_t)j * ts] = acc[j];
+            }
+            // S <- Diag(e^{Gamma_last}) S + Kt^T Delta
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const float4 g4 = lds_vec<float4>(&sm.gl[16 * m + 4 * grp]);
+                S[m][0] *= g4.x;
+                S[m][1] *= g4.y;
+                S[m][2] *= g4.z;
+                S[m][3] *= g4.w;
+                const f16x4 kh = lds_vec<f16x4>(&sm.KtT[0][16 * m + l16][4 * grp]);
+                const f16x4 kl = lds_vec<f16x4>(&sm.KtT[1][16 * m + l16][4 * grp]);
+                S[m] = mfma16k(kh, DBh, S[m]);
+                S[m] = mfma16k(kh, DBl, S[m]);
+                S[m] = mfma16k(kl, DBh, S[m]);
+            }
+        }
+        __syncthreads();
+    }
+
+    if (a.hT) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                a.hT[sbase + (uint32_t)(16 * m + 4 * grp + j) * D + vc] = S[m][j];
+    }
+}
+
+}  // namespace c16
+
+hipError_t launch_fwd_chunk16(const FwdArgs& a, hipStream_t stream) {
+    const int grid = ((a.nchains + 7) / 8) * 8 * c16::P;
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL(c16::kda_fwd_chunk16, dim3(grid), dim3(c16::NT), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace kda

@@ -108,7 +108,8 @@ struct alignas(16) Ops {
 // (Gamma_ref): the key and query factors of A and M. Rows at srow().
 struct alignas(16) Smem {
     Ops op[2];
-    __bf16 Ka[ROWS32];              // k * exp(Gamma_r - Gamma_ref), rounded to nearest
+    __bf16 Kah[ROWS32];             // k * exp(Gamma_r - Gamma_ref) = Kah + Kal
+    __bf16 Kal[ROWS32];
     __bf16 Kbh[ROWS32];             // k * exp(Gamma_ref - Gamma_r) = Kbh + Kbl
     __bf16 Kbl[ROWS32];
     __bf16 Qah[ROWS32];             // q * exp(Gamma_r - Gamma_ref) = Qah + Qal
@@ -265,10 +266,12 @@ __device__ __forceinline__ void factors(Smem& sm, Ops& op, HFetch& f, HStage& hs
             qa[ch][t] = qv[ch][t] * e1;
             kb[ch][t] = kv[ch][t] * e2;
         }
-        uint32_t kbh, kbl, qah, qal;
+        uint32_t kah, kal, kbh, kbl, qah, qal;
+        split_bf16x2(ka[0][t], ka[1][t], kah, kal);
         split_bf16x2(kb[0][t], kb[1][t], kbh, kbl);
         split_bf16x2(qa[0][t], qa[1][t], qah, qal);
-        *reinterpret_cast<uint32_t*>(&sm.Ka[so]) = pack_bf16(ka[0][t], ka[1][t]);
+        *reinterpret_cast<uint32_t*>(&sm.Kah[so]) = kah;
+        *reinterpret_cast<uint32_t*>(&sm.Kal[so]) = kal;
         *reinterpret_cast<uint32_t*>(&sm.Kbh[so]) = kbh;
         *reinterpret_cast<uint32_t*>(&sm.Kbl[so]) = kbl;
         *reinterpret_cast<uint32_t*>(&sm.Qah[so]) = qah;
@@ -346,8 +349,8 @@ __device__ __forceinline__ void store_tile(_Float16 (*hi)[TP], _Float16 (*lo)[TP
     }
 }
 
-// Helpers, step 2: the gated K K^T blocks of A (two-term keys) and the gated
-// Q K^T blocks of M (three terms), bf16 MFMA with fp32 accumulation:
+// Helpers, step 2: the gated K K^T blocks of A and the gated Q K^T blocks of
+// M, each from two-term bf16 factors (three MFMA terms), fp32 accumulation:
 //   hw 0: A00   hw 1: A11   hw 2: A10   hw 3: M00   hw 4: M10   hw 5: M11
 // A00 and A11 go to the state waves in fp32 (they invert I + A there); A10 and
 // M as fp16 operands. The zero blocks of Tm, A10 and M are written once, at
@@ -355,18 +358,23 @@ __device__ __forceinline__ void store_tile(_Float16 (*hi)[TP], _Float16 (*lo)[TP
 __device__ __forceinline__ void tiles(Smem& sm, Ops& op, const HStage& hs, int hw, int lane) {
     const int l16 = lane & 15, grp = lane >> 4;
     if (hw <= 2) {
-        // A[r][i] = beta_r (Ka_r . Kb_i): lane holds column i = l16 of rows r = 4grp + j
+        // A[r][i] = beta_r (Ka_r . Kb_i) = beta_r (Kah Kbh + Kah Kbl + Kal Kbh):
+        // lane holds column i = l16 of rows r = 4grp + j
         const int rb = hw == 0 ? 0 : 16, cb = hw == 1 ? 16 : 0;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = acc;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc1 = acc, acc2 = acc;
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
             const int ko = 32 * kk + 8 * grp;
-            const bf16x8 ka = lds_vec<bf16x8>(&sm.Ka[srow(rb + l16) + ko]);
-            acc = mfma16(ka, lds_vec<bf16x8>(&sm.Kbh[srow(cb + l16) + ko]), acc);
-            acc2 = mfma16(ka, lds_vec<bf16x8>(&sm.Kbl[srow(cb + l16) + ko]), acc2);
+            const bf16x8 kah = lds_vec<bf16x8>(&sm.Kah[srow(rb + l16) + ko]);
+            const bf16x8 kal = lds_vec<bf16x8>(&sm.Kal[srow(rb + l16) + ko]);
+            const bf16x8 kbh = lds_vec<bf16x8>(&sm.Kbh[srow(cb + l16) + ko]);
+            const bf16x8 kbl = lds_vec<bf16x8>(&sm.Kbl[srow(cb + l16) + ko]);
+            acc = mfma16(kah, kbh, acc);
+            acc1 = mfma16(kah, kbl, acc1);
+            acc2 = mfma16(kal, kbh, acc2);
         }
         state_operands(op, hs, hw, lane);   // VALU work while the products finish
-        acc += acc2;
+        acc += acc1 + acc2;
         if (hw < 2) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {

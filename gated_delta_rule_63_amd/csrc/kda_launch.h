@@ -56,6 +56,9 @@ hipError_t launch_fwd_serial(const FwdArgs& a, bool f32_inputs, hipStream_t stre
 int pipe_state_waves(int nchains, int cus);
 int pipe_workgroups(int nchains, int state_waves);
 hipError_t launch_fwd_pipe(const FwdArgs& a, int cus, hipStream_t stream);
+// The one-phase-at-a-time kernel with 16-token chunks (bf16 inputs): the
+// chunk-length ablation.
+hipError_t launch_fwd_chunk16(const FwdArgs& a, hipStream_t stream);
 // One recurrence step per (sequence, head) (T = 1, no cu): the decode step.
 // o, h0 and hT must be 16-byte aligned.
 hipError_t launch_decode(const FwdArgs& a, bool f32_inputs, hipStream_t stream);

@@ -129,6 +129,34 @@ kda_status_t kda_gdn_fwd(const void* q, const void* k, const void* v, const floa
                          void* o, float* hT, const kda_desc_t* desc, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * One forward kernel by name, for comparisons and ablations. Arguments,
+ * layouts, aliasing and errors as kda_fwd; `kernel` is a kda_kernel_t.
+ *   KDA_KERNEL_AUTO     what kda_fwd runs (including its decode and slice routes).
+ *   KDA_KERNEL_PIPE     32-token chunks; helper waves form chunk i+1's operands
+ *                       while state waves advance chunk i (bf16 inputs only).
+ *   KDA_KERNEL_SERIAL   32-token chunks; the four steps of a chunk (gate scan,
+ *                       A/M blocks and inverse, state products, output) one after
+ *                       another in four waves. kda_fwd uses it for fp32 inputs.
+ *   KDA_KERNEL_CHUNK16  as SERIAL with 16-token chunks: one 16 x 16 block per
+ *                       chunk, the chunk length FlashKDA's v1 chose for its bf16
+ *                       range and cheap inverse (toolarium.ru page, section "Где
+ *                       ограничения прямо сейчас"); bf16 inputs only.
+ * All give the same result within rounding (no kernel changes the method).
+ * An unknown value, or PIPE / CHUNK16 with fp32 inputs, is KDA_ERR_UNSUPPORTED.
+ * None of them needs a workspace. */
+typedef enum {
+    KDA_KERNEL_AUTO = 0,
+    KDA_KERNEL_PIPE = 1,
+    KDA_KERNEL_SERIAL = 2,
+    KDA_KERNEL_CHUNK16 = 3
+} kda_kernel_t;
+
+kda_status_t kda_fwd_kernel(const void* q, const void* k, const void* v, const float* g,
+                            const float* beta, const int32_t* cu_seqlens, const float* h0,
+                            void* o, float* hT, const kda_desc_t* desc, int32_t kernel,
+                            void* stream);
+
+/* ---------------------------------------------------------------------------
  * Decode step: one new token for each of N sequences, i.e. one step of the
  * recurrence above per (sequence, head), applied to a state carried over from
  * a prefill (the pages list decode as the next, not yet tuned, part of the

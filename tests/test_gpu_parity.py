@@ -104,3 +104,13 @@ def test_c4_sampled_heads():
     log("[full] T131072_H32: generating inputs")
     inp = W.make_inputs(W.CONFIGS["T131072_H32"], 0)
     check(inp, heads=[0, 9, 22, 31], what="T131072_H32 heads 0,9,22,31")
+
+
+@pytest.mark.parametrize("seed", [3, 7, 11])
+def test_one_hot_keys_seeds(seed):
+    """With one-hot keys every entry of A comes from a single channel, so no sum
+    over channels dilutes the rounding of its factors: a key factor rounded once
+    to bf16 (relative error up to 2^-9) shows in hT at about 1e-2 RMS. Both
+    factors of A are two-term splits, which keeps it near 2e-3."""
+    cfg = W.variant("T8192_H96", T=300, H=2, keys="onehot", h0=True, gate="mild", name="one-hot keys")
+    check(W.make_inputs(cfg, seed), dtype="bf16", what=f"one-hot keys seed {seed}")
