@@ -76,6 +76,18 @@ def test_fwd_rejects_before_launch(K):
     assert K.lib().kda_stage_output(P, ctypes.byref(d), None) == -5                       # too small
 
 
+def test_fwd_kernel_rejects_before_launch(K):
+    """kda_fwd_kernel: an unknown kernel, or a bf16-only kernel with fp32 inputs,
+    is KDA_ERR_UNSUPPORTED; shape errors as kda_fwd. All before any launch."""
+    L = K.lib()
+    run = lambda d, kern: L.kda_fwd_kernel(P, P, P, P, P, None, None, P, None, ctypes.byref(d), kern, None)
+    assert run(desc(K), 4) == -3 and run(desc(K), -1) == -3
+    assert run(desc(K, in_dt=1), K.KERNELS["pipe"]) == -3
+    assert run(desc(K, in_dt=1), K.KERNELS["chunk16"]) == -3
+    assert run(desc(K, Kd=64), K.KERNELS["serial"]) == -3
+    assert run(desc(K, N=3), K.KERNELS["chunk16"]) == -2
+
+
 def test_decode_rejects_before_launch(K):
     """kda_decode_step: shape, null and alignment errors return before any launch."""
     L = K.lib()
