@@ -174,9 +174,10 @@ def main():
                     help="extra repeats of --steps iterations (the pages' 30/200/5 protocol)")
     ap.add_argument("--path", choices=["fused", "staged"], default="fused",
                     help="fused: kda_fwd (the hot path); staged: kda_fwd_staged (five kernels)")
-    ap.add_argument("--kernel", choices=["auto", "pipe", "serial", "chunk16"], default="auto",
+    ap.add_argument("--kernel", choices=["auto", "pipe", "serial", "chunk16", "two_pass"], default="auto",
                     help="fused path: run this one forward kernel (kda_fwd_kernel); chunk16 is the "
-                         "16-token-chunk ablation of the serial kernel")
+                         "16-token-chunk ablation of the serial kernel, two_pass the two-kernel form "
+                         "of the pipelined one (its workspace allocated once, outside the timed steps)")
     ap.add_argument("--stages", action="store_true", help="also time each staged-path kernel on its own")
     ap.add_argument("--decode", type=int, default=0, metavar="N",
                     help="time the in-place decode step for N sequences (H = 96) instead of the prefill")
@@ -219,8 +220,12 @@ def main():
     hT = torch.empty((cfg.N, cfg.H, 128, 128), dtype=torch.float32, device=dev)
 
     if args.path == "fused":
+        nws = kda.kernel_workspace_size(q, args.kernel, cu) if args.kernel != "auto" else 0
+        ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+
         def step():
-            kda.fwd(q, k, v, g, beta, cu_seqlens=cu, initial_state=h0, out=o, final_state=hT, kernel=args.kernel)
+            kda.fwd(q, k, v, g, beta, cu_seqlens=cu, initial_state=h0, out=o, final_state=hT, kernel=args.kernel,
+                    workspace=ws)
     else:
         st = kda.Staged(q, k, v, g, beta, cu_seqlens=cu, initial_state=h0)
 
@@ -304,7 +309,8 @@ def main():
     elif args.kernel == "auto":
         kname = "kda_fwd_pipe" if cfg.dtype == "bf16" else "kda_fwd_fused (serial)"
     else:
-        kname = {"pipe": "kda_fwd_pipe", "serial": "kda_fwd_fused (serial)", "chunk16": "kda_fwd_chunk16"}[args.kernel]
+        kname = {"pipe": "kda_fwd_pipe", "serial": "kda_fwd_fused (serial)", "chunk16": "kda_fwd_chunk16",
+                 "two_pass": "kda_prep_pipe + kda_recur_pipe"}[args.kernel]
     # the counter summary covers the pipelined kernel as kda_fwd runs it
     traffic = traffic_from_profile(cfg.name) if (kname == "kda_fwd_pipe" and args.kernel == "auto") else None
 

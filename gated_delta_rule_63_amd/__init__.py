@@ -16,7 +16,7 @@ import torch
 
 from ._lib import KDA_BF16, KDA_F32, KERNELS, Desc, KDAError, Layout, lib, status_string  # noqa: F401
 
-__all__ = ["fwd", "gdn_fwd", "decode_step", "fwd_staged", "Staged", "KDAError", "status_string", "version"]
+__all__ = ["fwd", "gdn_fwd", "kernel_workspace_size", "decode_step", "fwd_staged", "Staged", "KDAError", "status_string", "version"]
 
 D = 128
 
@@ -59,22 +59,28 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
         output_final_state: bool = True, out: Optional[torch.Tensor] = None,
         final_state: Optional[torch.Tensor] = None,
         stream: Optional[torch.cuda.Stream] = None,
-        kernel: str = "auto") -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+        kernel: str = "auto", workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """KDA chunked forward. Shapes: q, k, v, g [B, T, H, 128]; beta [B, T, H];
     cu_seqlens int32 [N + 1] (B == 1); initial_state / final state [N, H, 128, 128] fp32.
 
     Returns (o fp32 [B, T, H, 128], hT or None). Tensors must be contiguous and on
     one GPU; q, k, v share a dtype (bf16 or fp32); g and beta are fp32.
-    kernel: "auto" (kda_fwd), or "pipe", "serial", "chunk16" to run that one
-    forward kernel (kda_fwd_kernel).
+    kernel: "auto" (kda_fwd), or "pipe", "serial", "chunk16", "two_pass" to run
+    that one forward kernel (kda_fwd_kernel). workspace: an optional device
+    tensor handed over as desc->workspace (see kernel_workspace_size).
     """
     if kernel == "auto":
         return _forward("kda_fwd", q, k, v, g, beta, cu_seqlens, initial_state, output_final_state,
-                        out, final_state, stream)
+                        out, final_state, stream, workspace=workspace)
     if kernel not in KERNELS:
         raise ValueError(f"kernel must be one of {sorted(KERNELS)}")
     return _forward("kda_fwd_kernel", q, k, v, g, beta, cu_seqlens, initial_state, output_final_state,
-                    out, final_state, stream, KERNELS[kernel])
+                    out, final_state, stream, ctypes.c_int32(KERNELS[kernel]), workspace=workspace)
+
+
+def kernel_workspace_size(q: torch.Tensor, kernel: str, cu_seqlens: Optional[torch.Tensor] = None) -> int:
+    """Bytes of device workspace fwd(..., kernel=kernel) uses (0: none)."""
+    return int(lib().kda_fwd_kernel_workspace_size(ctypes.byref(_desc(q, cu_seqlens)), KERNELS[kernel]))
 
 
 def gdn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
@@ -89,9 +95,14 @@ def gdn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, 
 
 
 def _forward(entry, q, k, v, g, beta, cu_seqlens, initial_state, output_final_state, out, final_state,
-             stream, *extra):
+             stream, *extra, workspace=None):
     _check_inputs(q, k, v, g, beta, cu_seqlens, scalar_gate=(entry == "kda_gdn_fwd"))
     d = _desc(q, cu_seqlens)
+    if workspace is not None:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous device tensor")
+        d.workspace = workspace.data_ptr()
+        d.workspace_bytes = workspace.numel() * workspace.element_size()
     B, T, H, _ = q.shape
     if initial_state is not None:
         if initial_state.dtype != torch.float32 or not initial_state.is_contiguous() \

@@ -9,12 +9,13 @@ LIB_PATH = os.path.join(HERE, "libkda.so")
 
 KDA_BF16, KDA_F32 = 0, 1
 # kda_kernel_t
-KERNELS = {"auto": 0, "pipe": 1, "serial": 2, "chunk16": 3}
+KERNELS = {"auto": 0, "pipe": 1, "serial": 2, "chunk16": 3, "two_pass": 4}
 STATUS = {0: "KDA_OK", -1: "KDA_ERR_NULL", -2: "KDA_ERR_SHAPE", -3: "KDA_ERR_UNSUPPORTED",
           -4: "KDA_ERR_DTYPE", -5: "KDA_ERR_WORKSPACE", -6: "KDA_ERR_HIP"}
 
 # every symbol include/kda.h declares
 EXPORTS = ["kda_status_string", "kda_version", "kda_fwd_check", "kda_fwd", "kda_gdn_fwd", "kda_fwd_kernel",
+           "kda_fwd_kernel_workspace_size",
            "kda_decode_step", "kda_staged_layout",
            "kda_fwd_workspace_size", "kda_stage_chunk_map", "kda_stage_gate_scan", "kda_stage_intra",
            "kda_stage_recurrence", "kda_stage_output", "kda_fwd_staged"]
@@ -61,6 +62,8 @@ def lib():
         L.kda_gdn_fwd.restype = ctypes.c_int
         L.kda_fwd_kernel.argtypes = [P] * 9 + [ctypes.POINTER(Desc), ctypes.c_int32, P]
         L.kda_fwd_kernel.restype = ctypes.c_int
+        L.kda_fwd_kernel_workspace_size.argtypes = [ctypes.POINTER(Desc), ctypes.c_int32]
+        L.kda_fwd_kernel_workspace_size.restype = ctypes.c_size_t
         L.kda_decode_step.argtypes = [P] * 8 + [ctypes.POINTER(Desc), P]
         L.kda_decode_step.restype = ctypes.c_int
         L.kda_fwd_workspace_size.argtypes = [ctypes.POINTER(Desc)]

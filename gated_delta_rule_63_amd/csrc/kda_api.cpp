@@ -146,6 +146,29 @@ hipError_t run_slices(const kda::FwdArgs& a, const kda_desc_t* d, int cus, hipSt
     return e;
 }
 
+// The two-kernel form: operand records in desc->workspace when it is large
+// enough, else in a stream-ordered allocation freed on the same stream.
+kda_status_t run_two_pass(const kda::FwdArgs& a, const kda_desc_t* d, int cus, hipStream_t s) {
+    const size_t bytes = kda::two_pass_workspace(a.nchains, d->T);
+    void* ws = nullptr;
+    bool owned = false;
+    if (d->workspace && d->workspace_bytes >= bytes) {
+        ws = d->workspace;
+    } else if (bytes > 0) {
+        if (hipMallocAsync(&ws, bytes, s) != hipSuccess) {
+            (void)hipGetLastError();
+            return KDA_ERR_WORKSPACE;
+        }
+        owned = true;
+    }
+    hipError_t e = kda::launch_fwd_two_pass(a, ws, cus, s);
+    if (owned) {
+        const hipError_t ef = hipFreeAsync(ws, s);
+        if (e == hipSuccess) e = ef;
+    }
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 // Chooses the kernel for a forward pass (kda_fwd and kda_gdn_fwd).
 kda_status_t run_fwd(const kda::FwdArgs& a, const kda_desc_t* desc, const void* o, const float* h0,
                      const float* hT, bool varlen, void* stream) {
@@ -277,17 +300,25 @@ kda_status_t kda_fwd_kernel(const void* q, const void* k, const void* v, const f
     const kda_status_t st = check(q, k, v, g, beta, cu_seqlens, o, desc);
     if (st != KDA_OK) return st;
     const bool f32 = desc->in_dtype == KDA_F32;
-    if (kernel < KDA_KERNEL_AUTO || kernel > KDA_KERNEL_CHUNK16) return KDA_ERR_UNSUPPORTED;
-    if (f32 && (kernel == KDA_KERNEL_PIPE || kernel == KDA_KERNEL_CHUNK16)) return KDA_ERR_UNSUPPORTED;
+    if (kernel < KDA_KERNEL_AUTO || kernel > KDA_KERNEL_TWO_PASS) return KDA_ERR_UNSUPPORTED;
+    if (f32 && kernel != KDA_KERNEL_AUTO && kernel != KDA_KERNEL_SERIAL) return KDA_ERR_UNSUPPORTED;
+    if (kernel == KDA_KERNEL_TWO_PASS && cu_seqlens) return KDA_ERR_UNSUPPORTED;
     const kda::FwdArgs a = fwd_args(q, k, v, g, beta, cu_seqlens, h0, o, hT, desc);
     if (kernel == KDA_KERNEL_AUTO) return run_fwd(a, desc, o, h0, hT, cu_seqlens != nullptr, stream);
     if (a.nchains == 0) return KDA_OK;
     const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (kernel == KDA_KERNEL_TWO_PASS) return run_two_pass(a, desc, device_cus(), s);
     hipError_t e;
     if (kernel == KDA_KERNEL_PIPE) e = kda::launch_fwd_pipe(a, device_cus(), s);
     else if (kernel == KDA_KERNEL_SERIAL) e = kda::launch_fwd_serial(a, f32, s);
     else e = kda::launch_fwd_chunk16(a, s);
     return hip_status(e);
+}
+
+size_t kda_fwd_kernel_workspace_size(const kda_desc_t* desc, int32_t kernel) {
+    if (!desc || kernel != KDA_KERNEL_TWO_PASS) return 0;
+    if (check_desc(desc, desc->num_seqs != desc->B) != KDA_OK) return 0;
+    return kda::two_pass_workspace(desc->num_seqs * desc->H, desc->T);
 }
 
 kda_status_t kda_decode_step(const void* q, const void* k, const void* v, const float* g,

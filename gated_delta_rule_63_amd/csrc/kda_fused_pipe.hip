@@ -63,7 +63,6 @@ static_assert(NH * 16 == D && NSEG * 8 == 64, "helper lanes: 8 channel pairs x 8
 // conflict-free. An array of R rows holds R * LDP + (R / 8 - 1) * SHIFT.
 __device__ __forceinline__ constexpr int srow(int r) { return r * LDP + (r >> 3) * SHIFT; }
 constexpr int ROWS32 = C * LDP + 3 * SHIFT;
-constexpr int ROWS16 = 16 * LDP + SHIFT;
 
 // 2^x as one v_exp_f32. Every argument here lies within [-120, 60] (log2
 // units of at most 24 decay steps with g >= -5) or underflows harmlessly:
@@ -719,7 +718,320 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
         }
     }
 }
+
+// ---------------------------------------------------------------------------
+// The same work as two kernels, the split the pages credit to FlashKDA (a
+// chunk-parallel preparation, then the sequential recurrence; toolarium.ru
+// page, section "Где ограничения прямо сейчас"), kept as an ablation of the
+// kernel count. The preparation writes every chunk's Ops to HBM and the
+// recurrence reads it back, so the arithmetic is the fused kernel's, value
+// for value; only the place where the operands wait between the halves moves
+// from LDS to HBM (about 1.2 KB more traffic per token-head each way).
+
+static_assert(sizeof(Ops) % 16 == 0, "records are copied in 16-byte pieces");
+constexpr int OPS_VEC = (int)(sizeof(Ops) / 16);   // 16-byte pieces per record
+// Copy waves of the recurrence kernel, and the record layout they move.
+constexpr int NCW = 4;
+constexpr int CG_LANES = 64 * (NCW / 2);                            // lanes of one copy group
+constexpr int CG_REGS = (OPS_VEC + CG_LANES - 1) / CG_LANES;        // 16-byte pieces per copy lane
+// Records are padded to a whole number of pieces per copy lane, so the copy
+// loops need no per-piece bounds (which would put each load in its own branch
+// and make the compiler wait for it there). The pad is never read.
+constexpr int REC_PIECES = CG_REGS * CG_LANES;
+struct alignas(16) OpsBuf {
+    Ops op;
+    uint4 pad[REC_PIECES - OPS_VEC];
+};
+static_assert(sizeof(OpsBuf) == 16 * REC_PIECES, "one record per operand buffer");
+
+// A copy lane's pieces of one record: src[0], src[CG_LANES], ... (global), and
+// the same positions of an operand buffer (LDS). Native vectors, so the
+// pieces stay in registers.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void rec_load(u32x4 (&r)[CG_REGS], const u32x4* src) {
+#pragma unroll
+    for (int k = 0; k < CG_REGS; ++k) r[k] = src[CG_LANES * k];
+}
+__device__ __forceinline__ void rec_store(const u32x4 (&r)[CG_REGS], u32x4* dst) {
+#pragma unroll
+    for (int k = 0; k < CG_REGS; ++k) dst[CG_LANES * k] = r[k];
+}
+
+// Workgroups of the preparation: chunks [g * prep_chunks, (g + 1) * prep_chunks)
+// of one (sequence, head), eight helper waves, fixed-length batches.
+__global__ __launch_bounds__(64 * NH, 1) void kda_prep_pipe(FwdArgs a, uint4* rec, int nch, int per_wg) {
+    __shared__ Smem sm;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int hw = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, grp = lane >> 4;
+    const int ngrp = (nch + per_wg - 1) / per_wg;
+    const int chain = blockIdx.x / ngrp;
+    if (chain >= a.nchains) return;
+    const int c_begin = (blockIdx.x % ngrp) * per_wg;
+    const int c_end = min(nch, c_begin + per_wg);
+    const int n = chain / a.H, h = chain % a.H;
+    const int t0 = 0, t1 = a.T;
+    const uint32_t ts = (uint32_t)a.H * D;
+    const long long base = (long long)n * a.T * ts + (long long)h * D;
+    const long long bbase = (long long)n * a.T * a.H + h;
+
+    // the never-written zero blocks of both operand buffers (as in the fused kernel)
+    for (int i = tid; i < 2 * C * 8; i += 64 * NH) {
+        const int bsel = i / (C * 8), r = (i / 8) % C, c = 2 * (i % 8);
+        const int col = kperm((r < 16 ? 16 : 0) + c);
+        Ops& op = sm.op[bsel];
+        *reinterpret_cast<uint32_t*>(&op.Tm[r][col]) = 0u;
+        if (r < 16) {
+            *reinterpret_cast<uint32_t*>(&op.M[0][r][col]) = 0u;
+            *reinterpret_cast<uint32_t*>(&op.M[1][r][col]) = 0u;
+            *reinterpret_cast<uint32_t*>(&op.A10[r][col]) = 0u;
+        }
+    }
+    const int cp = lane & 7, seg = lane >> 3;
+    const uint32_t coff = 16 * hw + 2 * cp;
+    float wpre[NSEG - 1];
+#pragma unroll
+    for (int s = 0; s < NSEG - 1; ++s)
+        wpre[s] = (s >= seg && s < NSEG / 2) ? -1.f : ((s >= NSEG / 2 && s < seg) ? 1.f : 0.f);
+    HOffs offs;
+#pragma unroll
+    for (int t = 0; t < SEG; ++t) {
+        offs.kq[t] = ((uint32_t)(SEG * seg + t) * ts + coff) * 2u;
+        offs.gg[t] = 2u * offs.kq[t];
+    }
+    offs.b = (uint32_t)(SEG * seg + (cp & 3)) * (uint32_t)a.H * 4u;
+    HFetch f;
+    HStage hs;
+    __syncthreads();
+    if (c_begin < c_end) {
+        const int cs = t0 + c_begin * C;
+        hfetch<false>(f, a, base + (long long)cs * ts, bbase + (long long)cs * a.H, ts, min(C, t1 - cs), offs);
+    }
+    for (int ci = c_begin; ci < c_end; ++ci) {
+        Ops& op = sm.op[ci & 1];
+        const int cs = t0 + ci * C;
+        const bool more = ci + 1 < c_end;
+        const int nnv = more ? min(C, t1 - cs - C) : 0;
+        factors<false>(sm, op, f, hs, hw, lane, wpre, more, a, base + (long long)(cs + C) * ts,
+                       bbase + (long long)(cs + C) * a.H, ts, offs, nnv);
+        __syncthreads();
+        tiles(sm, op, hs, hw, lane);
+        __syncthreads();
+        if (hw < 2) invert_block(op, hw, l16, grp);
+        __syncthreads();
+        const uint4* src = reinterpret_cast<const uint4*>(&op);
+        uint4* dst = rec + ((size_t)chain * nch + ci) * REC_PIECES;
+        for (int i = tid; i < OPS_VEC; i += 64 * NH) dst[i] = src[i];
+    }
+}
+
+// The recurrence: NS state waves as in the fused kernel (the inverses now come
+// with the record), and NCW copy waves that write chunk i+1's record into the
+// other operand buffer while the state waves advance chunk i. One workgroup
+// barrier per chunk.
+
+// One workgroup per CU is the target (its LDS would allow two): the copy lanes
+// hold a whole record piece set in registers.
+template <int NS>
+__global__ __launch_bounds__(64 * (NS + NCW), 1) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void kda_recur_pipe(FwdArgs a, const uint4* rec, int nch) {
+    constexpr int VB = Split<NS>::VB, P = Split<NS>::P;
+    __shared__ OpsBuf ops[2];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, grp = lane >> 4;
+    const int bid = blockIdx.x;
+    const int xcd = bid & 7, rest = bid >> 3;
+    const int vblk = rest % P;
+    const int chain = (rest / P) * 8 + xcd;
+    if (chain >= a.nchains) return;
+    const int n = chain / a.H, h = chain % a.H;
+    const int t0 = 0, t1 = a.T;
+    const uint32_t ts = (uint32_t)a.H * D;
+    const long long base = (long long)n * a.T * ts + (long long)h * D;
+    const long long sbase = ((long long)n * a.H + h) * D * D;
+    const uint4* crec = rec + (size_t)chain * nch * REC_PIECES;
+
+    if (wave < NS) {
+        const int vc = vblk * VB + wave * 16 + l16;
+        uint32_t voff[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) voff[i] = ((uint32_t)(16 * (i >> 2) + 4 * grp + (i & 3)) * ts + vc) * 2u;
+        f32x4 S[8];
+        uint32_t vcur[8], vnxt[8];
+        auto vfetch = [&](uint32_t* dst, int cidx) {
+            const int cs = t0 + cidx * C;
+            const auto rv = chunk_rsrc(a.v, base + (long long)cs * ts, 2, min(C, t1 - cs), ts, D);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) dst[i] = __builtin_amdgcn_raw_buffer_load_b16(rv, voff[i], 0, 0);
+        };
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                S[m][j] = a.h0 ? a.h0[sbase + (uint32_t)(16 * m + 4 * grp + j) * D + vc] : 0.f;
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __builtin_amdgcn_s_setprio(2);
+        if (nch > 0) {
+            vfetch(vnxt, 0);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) vcur[j] = vnxt[j];
+        }
+        __syncthreads();   // record 0 is in ops[0]
+        for (int ci = 0; ci < nch; ++ci) {
+            const int cs = t0 + ci * C;
+            const int nv = min(C, t1 - cs);
+            const Ops& op = ops[ci & 1].op;
+            if (ci + 1 < nch) vfetch(vnxt, ci + 1);
+            f16x8 SBh[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                uint32_t w[4];
+                w[0] = pack_f16(S[2 * kk][0], S[2 * kk][1]);
+                w[1] = pack_f16(S[2 * kk][2], S[2 * kk][3]);
+                w[2] = pack_f16(S[2 * kk + 1][0], S[2 * kk + 1][1]);
+                w[3] = pack_f16(S[2 * kk + 1][2], S[2 * kk + 1][3]);
+                SBh[kk] = __builtin_bit_cast(f16x8, w);
+            }
+            f32x4 Pt[2], Ot[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                Pt[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                Ot[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const int off = srow(16 * t + l16) + 32 * kk + 8 * grp;
+                    Pt[t] = mfma16(lds_vec<f16x8>(&op.Kg[off]), SBh[kk], Pt[t]);
+                    Ot[t] = mfma16(lds_vec<f16x8>(&op.Qg[off]), SBh[kk], Ot[t]);
+                }
+            }
+            const float4 bt0 = lds_vec<float4>(&op.beta[4 * grp]), bt1 = lds_vec<float4>(&op.beta[16 + 4 * grp]);
+            const f16x8 ah = lds_vec<f16x8>(&op.A10[l16][8 * grp]);
+            const float bts[2][4] = {{bt0.x, bt0.y, bt0.z, bt0.w}, {bt1.x, bt1.y, bt1.z, bt1.w}};
+            float be[2][4];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    be[t][j] = bts[t][j] * (__uint_as_float(vcur[4 * t + j] << 16) - Pt[t][j]);
+            uint32_t bh[4] = {0u, 0u, 0u, 0u}, bl[4] = {0u, 0u, 0u, 0u};
+            split_f16x2(be[0][0], be[0][1], bh[0], bl[0]);
+            split_f16x2(be[0][2], be[0][3], bh[1], bl[1]);
+            f32x4 D0 = {0.f, 0.f, 0.f, 0.f};
+            {
+                const f16x8 th = lds_vec<f16x8>(&op.Tm[l16][8 * grp]);
+                D0 = mfma16(th, __builtin_bit_cast(f16x8, bh), D0);
+                D0 = mfma16(th, __builtin_bit_cast(f16x8, bl), D0);
+            }
+            uint32_t dh[4] = {0u, 0u, 0u, 0u}, dl[4] = {0u, 0u, 0u, 0u};
+            split_f16x2(D0[0], D0[1], dh[0], dl[0]);
+            split_f16x2(D0[2], D0[3], dh[1], dl[1]);
+            f32x4 X = {0.f, 0.f, 0.f, 0.f};
+            X = mfma16(ah, __builtin_bit_cast(f16x8, dh), X);
+            X = mfma16(ah, __builtin_bit_cast(f16x8, dl), X);
+            bh[0] = bh[1] = bl[0] = bl[1] = 0u;
+            split_f16x2(be[1][0] - X[0], be[1][1] - X[1], bh[2], bl[2]);
+            split_f16x2(be[1][2] - X[2], be[1][3] - X[3], bh[3], bl[3]);
+            f32x4 D1 = {0.f, 0.f, 0.f, 0.f};
+            {
+                const f16x8 th = lds_vec<f16x8>(&op.Tm[16 + l16][8 * grp]);
+                D1 = mfma16(th, __builtin_bit_cast(f16x8, bh), D1);
+                D1 = mfma16(th, __builtin_bit_cast(f16x8, bl), D1);
+            }
+            split_f16x2(D1[0], D1[1], dh[2], dl[2]);
+            split_f16x2(D1[2], D1[3], dh[3], dl[3]);
+            const f16x8 DBh = __builtin_bit_cast(f16x8, dh), DBl = __builtin_bit_cast(f16x8, dl);
+            const auto ro = chunk_rsrc(a.o, base + (long long)cs * ts, 4, nv, ts, D);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const f16x8 mh = lds_vec<f16x8>(&op.M[0][16 * t + l16][8 * grp]);
+                const f16x8 ml = lds_vec<f16x8>(&op.M[1][16 * t + l16][8 * grp]);
+                f32x4 acc = Ot[t];
+                acc = mfma16(mh, DBh, acc);
+                acc = mfma16(mh, DBl, acc);
+                acc = mfma16(ml, DBh, acc);
+                const float ov[4] = {acc[0], acc[1], acc[2], acc[3]};
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ov[j]), ro, 2u * voff[4 * t + j], 0, 0);
+            }
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const float4 g4 = lds_vec<float4>(&op.gl[16 * m + 4 * grp]);
+                S[m][0] *= g4.x;
+                S[m][1] *= g4.y;
+                S[m][2] *= g4.z;
+                S[m][3] *= g4.w;
+                const f16x8 kt = lds_vec<f16x8>(&op.KtT[16 * m + l16][8 * grp]);
+                S[m] = mfma16(kt, DBh, S[m]);
+                S[m] = mfma16(kt, DBl, S[m]);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) vcur[j] = vnxt[j];
+            __syncthreads();   // ops[ci & 1] is free, ops[(ci + 1) & 1] holds record ci+1
+        }
+        if (a.hT) {
+#pragma unroll
+            for (int m = 0; m < 8; ++m)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    a.hT[sbase + (uint32_t)(16 * m + 4 * grp + j) * D + vc] = S[m][j];
+        }
+    } else {
+        // Two copy groups of NCW / 2 waves: group g moves the records of
+        // parity g, so each group loads a record two chunks before it is due
+        // and the load has two chunk periods to arrive. Lane i of a group
+        // moves pieces i, i + CG_LANES, ... of a record.
+        const int cg = (wave - NS) / (NCW / 2);
+        const int cl = tid - 64 * NS - CG_LANES * cg;
+        const u32x4* src = reinterpret_cast<const u32x4*>(crec) + cl;
+        u32x4 r[CG_REGS];
+        if (cg == 0) {
+            if (nch > 0) {
+                rec_load(r, src);
+                rec_store(r, reinterpret_cast<u32x4*>(&ops[0]) + cl);
+                if (nch > 2) rec_load(r, src + 2 * (size_t)REC_PIECES);
+            }
+        } else if (nch > 1) {
+            rec_load(r, src + REC_PIECES);
+        }
+        __syncthreads();
+        for (int ci = 0; ci < nch; ++ci) {
+            const int rn = ci + 1;   // the record due in LDS by the end of this chunk
+            if ((rn & 1) == cg && rn < nch) {
+                rec_store(r, reinterpret_cast<u32x4*>(&ops[rn & 1]) + cl);
+                if (rn + 2 < nch) rec_load(r, src + (size_t)(rn + 2) * REC_PIECES);
+            }
+            __syncthreads();
+        }
+    }
+}
+
 }  // namespace pipe
+
+size_t two_pass_workspace(int nchains, int T) {
+    const size_t nch = (size_t)((T + pipe::C - 1) / pipe::C);
+    return (size_t)nchains * nch * sizeof(pipe::OpsBuf);
+}
+
+hipError_t launch_fwd_two_pass(const FwdArgs& a, void* workspace, int cus, hipStream_t stream) {
+    const int nch = (a.T + pipe::C - 1) / pipe::C;
+    if (a.nchains == 0) return hipSuccess;
+    uint4* rec = static_cast<uint4*>(workspace);
+    constexpr int per_wg = 16;
+    if (nch > 0) {
+        const int grid1 = a.nchains * ((nch + per_wg - 1) / per_wg);
+        hipLaunchKernelGGL(pipe::kda_prep_pipe, dim3(grid1), dim3(64 * pipe::NH), 0, stream, a, rec, nch, per_wg);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int ns = pipe_state_waves(a.nchains, cus);
+    const dim3 g3(pipe_workgroups(a.nchains, ns));
+    if (ns == 1) hipLaunchKernelGGL((pipe::kda_recur_pipe<1>), g3, dim3(64 * (1 + pipe::NCW)), 0, stream, a, rec, nch);
+    else if (ns == 2) hipLaunchKernelGGL((pipe::kda_recur_pipe<2>), g3, dim3(64 * (2 + pipe::NCW)), 0, stream, a, rec, nch);
+    else hipLaunchKernelGGL((pipe::kda_recur_pipe<4>), g3, dim3(64 * (4 + pipe::NCW)), 0, stream, a, rec, nch);
+    return hipGetLastError();
+}
 
 int pipe_state_waves(int nchains, int cus) {
     if ((long long)nchains * 8 <= cus) return 1;

@@ -59,6 +59,11 @@ hipError_t launch_fwd_pipe(const FwdArgs& a, int cus, hipStream_t stream);
 // The one-phase-at-a-time kernel with 16-token chunks (bf16 inputs): the
 // chunk-length ablation.
 hipError_t launch_fwd_chunk16(const FwdArgs& a, hipStream_t stream);
+// The pipelined kernel's work as two kernels (fixed-length bf16 batches): a
+// chunk-parallel preparation that writes every chunk's operands to
+// `workspace` (two_pass_workspace bytes), then the recurrence that reads them.
+size_t two_pass_workspace(int nchains, int T);
+hipError_t launch_fwd_two_pass(const FwdArgs& a, void* workspace, int cus, hipStream_t stream);
 // One recurrence step per (sequence, head) (T = 1, no cu): the decode step.
 // o, h0 and hT must be 16-byte aligned.
 hipError_t launch_decode(const FwdArgs& a, bool f32_inputs, hipStream_t stream);

@@ -141,15 +141,30 @@ kda_status_t kda_gdn_fwd(const void* q, const void* k, const void* v, const floa
  *                       chunk, the chunk length FlashKDA's v1 chose for its bf16
  *                       range and cheap inverse (toolarium.ru page, section "Где
  *                       ограничения прямо сейчас"); bf16 inputs only.
+ *   KDA_KERNEL_TWO_PASS PIPE's work as two kernels, the split the same section
+ *                       credits to FlashKDA: a chunk-parallel preparation writes
+ *                       every chunk's operands to device memory, then the
+ *                       recurrence reads them back. Same values as PIPE, bit for
+ *                       bit. bf16 inputs, no cu_seqlens. Needs
+ *                       kda_fwd_kernel_workspace_size() bytes of device memory:
+ *                       desc->workspace when at least that large, else a
+ *                       stream-ordered allocation on `stream`, freed on it
+ *                       (KDA_ERR_WORKSPACE if that fails).
  * All give the same result within rounding (no kernel changes the method).
- * An unknown value, or PIPE / CHUNK16 with fp32 inputs, is KDA_ERR_UNSUPPORTED.
- * None of them needs a workspace. */
+ * An unknown value, a bf16-only kernel with fp32 inputs, or TWO_PASS with
+ * cu_seqlens is KDA_ERR_UNSUPPORTED. Only TWO_PASS uses a workspace. */
 typedef enum {
     KDA_KERNEL_AUTO = 0,
     KDA_KERNEL_PIPE = 1,
     KDA_KERNEL_SERIAL = 2,
-    KDA_KERNEL_CHUNK16 = 3
+    KDA_KERNEL_CHUNK16 = 3,
+    KDA_KERNEL_TWO_PASS = 4
 } kda_kernel_t;
+
+/* Bytes of device workspace kda_fwd_kernel needs for `kernel` (0 when it
+ * needs none or the descriptor is invalid). TWO_PASS: one 40,960-byte record
+ * per (sequence, head, 32-token chunk). */
+size_t kda_fwd_kernel_workspace_size(const kda_desc_t* desc, int32_t kernel);
 
 kda_status_t kda_fwd_kernel(const void* q, const void* k, const void* v, const float* g,
                             const float* beta, const int32_t* cu_seqlens, const float* h0,

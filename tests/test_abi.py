@@ -81,7 +81,15 @@ def test_fwd_kernel_rejects_before_launch(K):
     is KDA_ERR_UNSUPPORTED; shape errors as kda_fwd. All before any launch."""
     L = K.lib()
     run = lambda d, kern: L.kda_fwd_kernel(P, P, P, P, P, None, None, P, None, ctypes.byref(d), kern, None)
-    assert run(desc(K), 4) == -3 and run(desc(K), -1) == -3
+    assert run(desc(K), 5) == -3 and run(desc(K), -1) == -3
+    assert run(desc(K, in_dt=1), K.KERNELS["two_pass"]) == -3
+    cu = ctypes.c_void_p(0x2000)
+    assert L.kda_fwd_kernel(P, P, P, P, P, cu, None, P, None, ctypes.byref(desc(K, N=3)), K.KERNELS["two_pass"],
+                            None) == -3                                   # two_pass takes no cu_seqlens
+    # one 40,960-byte operand record per (sequence, head, 32-token chunk)
+    size = lambda d, kern: L.kda_fwd_kernel_workspace_size(ctypes.byref(d), kern)
+    assert size(desc(K, B=2, T=100, H=3), K.KERNELS["two_pass"]) == 2 * 3 * 4 * 40960
+    assert size(desc(K), K.KERNELS["pipe"]) == 0 and size(desc(K, Kd=64), K.KERNELS["two_pass"]) == 0
     assert run(desc(K, in_dt=1), K.KERNELS["pipe"]) == -3
     assert run(desc(K, in_dt=1), K.KERNELS["chunk16"]) == -3
     assert run(desc(K, Kd=64), K.KERNELS["serial"]) == -3

@@ -75,8 +75,50 @@ def test_fp32_rejected_by_bf16_kernels():
     import gated_delta_rule_63_amd as kda
     cfg = W.variant("tiny_fp32", T=40, H=2, name="fp32 reject")
     t = to_device(W.make_inputs(cfg, 1, dtype="fp32"), "fp32")
-    for kernel in ("pipe", "chunk16"):
+    for kernel in ("pipe", "chunk16", "two_pass"):
         with pytest.raises(kda.KDAError):
             kda.fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], kernel=kernel)
     with pytest.raises(ValueError):
         kda.fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], kernel="chunk64")
+
+
+TWO_PASS_CASES = [
+    ("fixed T=1000 (ragged)", dict(T=1000, H=3)),
+    ("batch 2 T=333", dict(B=2, T=333, H=2, h0=True)),
+    ("mild decay with h0", dict(T=700, H=2, h0=True, gate="mild")),
+    ("single token", dict(T=1, H=2, h0=True)),
+    ("T=8192 H=96", dict()),
+]
+
+
+@pytest.mark.parametrize("what,kw", TWO_PASS_CASES, ids=[c[0] for c in TWO_PASS_CASES])
+def test_two_pass_equals_pipe_bitwise(what, kw):
+    """The two-kernel form runs the pipelined kernel's arithmetic with the
+    operands parked in device memory between the halves: identical o and hT."""
+    import torch
+    cfg = W.variant("T8192_H96", name=what, **kw)
+    inp = W.make_inputs(cfg, 13)
+    o1, h1 = run_kernel(inp, "bf16", "pipe")
+    o2, h2 = run_kernel(inp, "bf16", "two_pass")
+    log(f"[kernel two_pass] {what}: max|o - o_pipe| = {np.abs(o1 - o2).max():.3e}")
+    np.testing.assert_array_equal(o2, o1)
+    np.testing.assert_array_equal(h2, h1)
+    if cfg.T <= 1000:
+        ro, rs = run_oracle(inp)
+        assert rel_err(o2, ro) <= TOL["bf16"][0] and rel_err(h2, rs) <= TOL["bf16"][1]
+
+
+def test_two_pass_with_caller_workspace():
+    """A large enough desc->workspace is used instead of an allocation; the result is the same."""
+    import torch
+    import gated_delta_rule_63_amd as kda
+    cfg = W.variant("T8192_H96", T=600, H=3, h0=True, name="two_pass workspace")
+    inp = W.make_inputs(cfg, 14)
+    t = to_device(inp, "bf16")
+    nbytes = kda.kernel_workspace_size(t["q"], "two_pass")
+    assert nbytes == 3 * ((600 + 31) // 32) * 40960
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=t["q"].device)
+    o1, h1 = kda.fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], initial_state=t["h0"], kernel="two_pass", workspace=ws)
+    o2, h2 = kda.fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], initial_state=t["h0"], kernel="two_pass")
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
