@@ -187,7 +187,7 @@ def main():
                     help="run one device-to-device copy of this many MiB at the end (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "this benchmark runs on one GPU only (--gpus must be 1); the kernels shard by head across GPUs without communication, which is not implemented here",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
