@@ -86,6 +86,7 @@ TWO_PASS_CASES = [
     ("fixed T=1000 (ragged)", dict(T=1000, H=3)),
     ("batch 2 T=333", dict(B=2, T=333, H=2, h0=True)),
     ("mild decay with h0", dict(T=700, H=2, h0=True, gate="mild")),
+    ("17 chunks: one full preparation group and one of a single chunk", dict(T=530, H=2, h0=True)),
     ("single token", dict(T=1, H=2, h0=True)),
     ("T=8192 H=96", dict()),
 ]
