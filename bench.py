@@ -88,7 +88,24 @@ def bench_decode(args):
     g, beta = torch.from_numpy(inp.g).to(dev), torch.from_numpy(inp.beta).to(dev)
     state = torch.from_numpy(inp.h0).to(dev)
     o = torch.empty((N, 1, H, 128), dtype=torch.float32, device=dev)
-    step = lambda: kda.decode_step(q, k, v, g, beta, state=state, out=o, in_place=True)
+    one = lambda: kda.decode_step(q, k, v, g, beta, state=state, out=o, in_place=True)
+    step = one
+    G = args.graph
+    if G:
+        # G steps captured once and replayed: one graph launch per G steps, so
+        # the per-call cost of the binding and the launch is paid once per G
+        one()
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                for _ in range(G):
+                    one()
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize()
+        step = graph.replay
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -99,7 +116,7 @@ def bench_decode(args):
         step()
     e1.record(stream)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = e0.elapsed_time(e1) / args.steps / max(G, 1)
     per_head = 3 * 256 + 512 + 4 + 512 + 2 * STATE_BYTES
     bytes_ = N * H * per_head
     achieved = bytes_ / (ms / 1e3) / 1e9
@@ -108,7 +125,8 @@ def bench_decode(args):
         "value": N / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"decode: {N} sequences x {H} heads, one token each, fp32 state read and written",
+        "config": {"workload": f"decode: {N} sequences x {H} heads, one token each, fp32 state read and written"
+                               + (f", {G} steps per HIP graph launch" if G else ""),
                    "global_batch": N, "seq_len": 1, "heads": H, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "kda_decode_kernel",
@@ -181,6 +199,8 @@ def main():
     ap.add_argument("--stages", action="store_true", help="also time each staged-path kernel on its own")
     ap.add_argument("--decode", type=int, default=0, metavar="N",
                     help="time the in-place decode step for N sequences (H = 96) instead of the prefill")
+    ap.add_argument("--graph", type=int, default=0, metavar="G",
+                    help="with --decode: capture G decode steps in one HIP graph and time its replays")
     ap.add_argument("--gdn", action="store_true",
                     help="time the scalar-gate (Gated DeltaNet) forward at --config's shape instead")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
