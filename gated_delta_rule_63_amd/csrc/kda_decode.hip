@@ -5,10 +5,12 @@
 //
 // The state is the whole cost: 64 KiB read and 64 KiB written per (sequence,
 // head), against 1.3 KB of token inputs, so the kernel is HBM-bound and is
-// organised for one coalesced pass over S. One 256-thread workgroup per
-// (sequence, head); thread t holds rows 16*(t/32) .. +15 of columns
-// 4*(t%32) .. +3 in registers. The two column sums (S'^T k and S'^T q) are
-// reduced across the eight row groups through LDS; then
+// organised for one coalesced pass over S. A (sequence, head) is split over
+// CB workgroups of 128 / CB columns (CB = 4 when there are few sequences, so
+// that enough workgroups stream the state; 1 otherwise), each of 256 / CB
+// threads; thread t holds rows 16*(t/CG) .. +15 of four columns in registers
+// (CG = 32 / CB column groups of four). The two column sums (S'^T k and
+// S'^T q) are reduced across the eight row groups through LDS; then
 //   o = S'^T q + beta e (k . q)
 // needs no second pass, and each thread writes back exactly the block it read
 // (so the state may be updated in place).
@@ -18,13 +20,13 @@
 namespace kda {
 namespace decode {
 
-constexpr int NT = 256;
 constexpr int RG = 8;            // row groups of 16 rows
-constexpr int CG = 32;           // column groups of 4 columns
 
-template <bool F32>
-__global__ __launch_bounds__(NT) void kda_decode_kernel(FwdArgs a) {
-    const int nh = blockIdx.x;                 // sequence * H + head
+template <bool F32, int CB>
+__global__ __launch_bounds__(256 / CB) void kda_decode_kernel(FwdArgs a) {
+    constexpr int NT = 256 / CB;           // threads per workgroup
+    constexpr int CG = 32 / CB;            // column groups of 4 columns
+    const int nh = blockIdx.x / CB;        // sequence * H + head
     if (nh >= a.nchains) return;
     const int n = nh / a.H, h = nh % a.H;
     const int t = threadIdx.x, cg = t % CG, rg = t / CG;
@@ -34,14 +36,14 @@ __global__ __launch_bounds__(NT) void kda_decode_kernel(FwdArgs a) {
     __shared__ float sk[D], sq[D], sgam[D];
     __shared__ float4 pk[RG][CG], pq[RG][CG];
     __shared__ float pkq[RG];
-    if (t < D) {
-        sk[t] = ld_in<F32>(a.k, tok + t);
-        sq[t] = ld_in<F32>(a.q, tok + t);
-        sgam[t] = expf(a.scalar_gate ? a.g[(long long)n * a.H + h] : a.g[tok + t]);
+    for (int i = t; i < D; i += NT) {
+        sk[i] = ld_in<F32>(a.k, tok + i);
+        sq[i] = ld_in<F32>(a.q, tok + i);
+        sgam[i] = expf(a.scalar_gate ? a.g[(long long)n * a.H + h] : a.g[tok + i]);
     }
     // this thread's block of the state
     float4 s[16];
-    const int v0 = 4 * cg;
+    const int v0 = (blockIdx.x % CB) * (D / CB) + 4 * cg;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int c = 16 * rg + r;
@@ -95,10 +97,17 @@ __global__ __launch_bounds__(NT) void kda_decode_kernel(FwdArgs a) {
 
 hipError_t launch_decode(const FwdArgs& a, bool f32_inputs, hipStream_t stream) {
     if (a.nchains == 0) return hipSuccess;
-    if (f32_inputs)
-        hipLaunchKernelGGL(decode::kda_decode_kernel<true>, dim3(a.nchains), dim3(decode::NT), 0, stream, a);
-    else
-        hipLaunchKernelGGL(decode::kda_decode_kernel<false>, dim3(a.nchains), dim3(decode::NT), 0, stream, a);
+    // few (sequence, head) pairs: four workgroups each, so that four times as
+    // many workgroups stream the state
+    const bool split = a.nchains < 512;
+    const dim3 grid(split ? 4 * a.nchains : a.nchains);
+    if (f32_inputs) {
+        if (split) hipLaunchKernelGGL((decode::kda_decode_kernel<true, 4>), grid, dim3(64), 0, stream, a);
+        else hipLaunchKernelGGL((decode::kda_decode_kernel<true, 1>), grid, dim3(256), 0, stream, a);
+    } else {
+        if (split) hipLaunchKernelGGL((decode::kda_decode_kernel<false, 4>), grid, dim3(64), 0, stream, a);
+        else hipLaunchKernelGGL((decode::kda_decode_kernel<false, 1>), grid, dim3(256), 0, stream, a);
+    }
     return hipGetLastError();
 }
 
