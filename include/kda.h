@@ -33,6 +33,12 @@
  * hipStream_t; NULL is the default stream); no call synchronises the device
  * or copies device memory to the host.
  *
+ * Graph capture. Every call may be recorded into a HIP graph on `stream`: the
+ * library launches kernels only (no memset, no host synchronisation). The one
+ * allocation, kda_fwd's slice workspace for few long chains, is skipped when
+ * desc->workspace is large enough; kda_fwd_kernel with KDA_KERNEL_TWO_PASS
+ * likewise.
+ *
  * Aliasing. h0 == hT (the same pointer) is allowed: each state tile is read
  * before it is overwritten by the workgroup that owns it. Any other overlap
  * between outputs and inputs is undefined.
@@ -45,7 +51,8 @@
  * Edge cases. T = 0 or zero-length sequences are allowed: such a sequence has
  * no output rows and hT = h0 (or 0 without h0).
  *
- * Threads. Every entry point is thread-safe and keeps no global mutable state.
+ * Threads. Every entry point is thread-safe; the only global state is a cache
+ * of each device's compute-unit count, written atomically.
  */
 #ifndef KDA_H
 #define KDA_H
