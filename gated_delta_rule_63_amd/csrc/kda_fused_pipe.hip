@@ -27,7 +27,13 @@
 // The split into a chunk-parallel preparation and a sequential recurrence is
 // the pages' two-kernel design (toolarium.ru page, section "Где ограничения
 // прямо сейчас"); here the two run concurrently on one CU so that each input
-// byte crosses HBM once.
+// byte crosses HBM once. The same halves as two kernels (kda_prep_pipe,
+// kda_recur_pipe, at the end of this file) are kept as a measured ablation.
+//
+// Precision: the gated factors of A and M are two-term bf16 splits on both
+// sides (three MFMA terms per product, about 16 significant bits, fp32
+// range); the state waves' operands K*gamma, Q*gamma, Kt and the rounded S are
+// single fp16, and beta (V - P) and Delta two-term fp16.
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -726,7 +732,7 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
 // kernel count. The preparation writes every chunk's Ops to HBM and the
 // recurrence reads it back, so the arithmetic is the fused kernel's, value
 // for value; only the place where the operands wait between the halves moves
-// from LDS to HBM (about 1.2 KB more traffic per token-head each way).
+// from LDS to HBM (1.28 KB more traffic per token-head each way).
 
 static_assert(sizeof(Ops) % 16 == 0, "records are copied in 16-byte pieces");
 constexpr int OPS_VEC = (int)(sizeof(Ops) / 16);   // 16-byte pieces per record
@@ -757,8 +763,8 @@ __device__ __forceinline__ void rec_store(const u32x4 (&r)[CG_REGS], u32x4* dst)
     for (int k = 0; k < CG_REGS; ++k) dst[CG_LANES * k] = r[k];
 }
 
-// Workgroups of the preparation: chunks [g * prep_chunks, (g + 1) * prep_chunks)
-// of one (sequence, head), eight helper waves, fixed-length batches.
+// Workgroups of the preparation: chunks [g * per_wg, (g + 1) * per_wg) of one
+// (sequence, head), eight helper waves, fixed-length batches.
 __global__ __launch_bounds__(64 * NH, 1) void kda_prep_pipe(FwdArgs a, uint4* rec, int nch, int per_wg) {
     __shared__ Smem sm;
     const int tid = threadIdx.x, lane = tid & 63;
