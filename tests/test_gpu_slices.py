@@ -44,6 +44,21 @@ def test_sliced_chain_matches_oracle(gate, h0):
     assert eo <= tol_o and es <= tol_s
 
 
+def test_sliced_batch_with_ragged_tail():
+    """Two batch rows (six chains) whose length is not a whole number of chunks:
+    the slices' chain index covers the batch row, and the last slice ends in a
+    partial chunk."""
+    cfg = W.variant("T131072_H32", B=2, T=12301, H=3, gate="mild", h0=True, name="slices B=2 ragged")
+    inp = W.make_inputs(cfg, 13)
+    t = to_device(inp, "bf16")
+    o, hT = fwd(t)
+    ro, rs = run_oracle(inp)
+    eo, es = rel_err(o.cpu().numpy(), ro), rel_err(hT.cpu().numpy(), rs)
+    tol_o, tol_s = TOL["bf16"]
+    log(f"[slices] B=2 T=12301 H=3: err_o {eo:.2e} err_hT {es:.2e}")
+    assert eo <= tol_o and es <= tol_s
+
+
 def test_sliced_chain_state_alias():
     """h0 == hT (in place) through the sliced path: the first pass reads h0 before
     the last one writes hT."""
