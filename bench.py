@@ -72,6 +72,23 @@ def traffic_from_profile(workload: str):
     return float(m_b.group(1))
 
 
+def host_description() -> dict:
+    """The CPU the oracle baseline ran on: model name, logical CPUs and the
+    OpenMP thread setting."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(),
+            "sched_affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
+            "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}
+
+
 def bench_decode(args):
     """In-place decode steps: N sequences x 96 heads, one token each per step."""
     import numpy as np
@@ -346,7 +363,8 @@ def main():
             if dt >= 10.0 or runs >= 50:
                 break
         cpu = {"value": tokens * runs / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
-               "sample": f"the whole {cfg.name} workload ({cfg.token_heads} token-heads) {runs} times, {dt:.1f} s"}
+               "sample": f"the whole {cfg.name} workload ({cfg.token_heads} token-heads) {runs} times, {dt:.1f} s",
+               "host": host_description()}
 
     desc = f"{cfg.name}: B={cfg.B} T={cfg.T} H={cfg.H} K=V=128 {cfg.dtype} q/k/v, fp32 g/beta/state"
     if cfg.seq_lens:

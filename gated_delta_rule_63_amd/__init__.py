@@ -16,7 +16,7 @@ import torch
 
 from ._lib import KDA_BF16, KDA_F32, KERNELS, Desc, KDAError, Layout, lib, status_string  # noqa: F401
 
-__all__ = ["fwd", "gdn_fwd", "kernel_workspace_size", "decode_step", "fwd_staged", "Staged", "KDAError", "status_string", "version"]
+__all__ = ["fwd", "gdn_fwd", "fwd_workspace_size", "kernel_workspace_size", "decode_step", "fwd_staged", "Staged", "KDAError", "status_string", "version"]
 
 D = 128
 
@@ -36,10 +36,14 @@ def _desc(q: torch.Tensor, cu_seqlens: Optional[torch.Tensor]) -> Desc:
     return Desc(B, T, H, K, K, N, dt, KDA_F32, None, 0)
 
 
-def _check_inputs(q, k, v, g, beta, cu_seqlens, scalar_gate=False):
+def _check_inputs(q, k, v, g, beta, cu_seqlens, scalar_gate=False, _device=True):
+    """Raises ValueError unless the inputs are what the C ABI reads: contiguous
+    tensors on one GPU with the shapes and dtypes of include/kda.h. (_device=False
+    skips the GPU requirement only, so the checks can be exercised on the CPU.)"""
+    dev = q.device
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous device tensor")
+        if (_device and not t.is_cuda) or not t.is_contiguous() or t.device != dev:
+            raise ValueError(f"{name} must be a contiguous device tensor on q's device")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share a dtype")
     if g.dtype != torch.float32 or beta.dtype != torch.float32:
@@ -50,8 +54,26 @@ def _check_inputs(q, k, v, g, beta, cu_seqlens, scalar_gate=False):
         raise ValueError("g must be [B, T, H]" if scalar_gate else "g must be [B, T, H, 128]")
     if beta.shape != q.shape[:3]:
         raise ValueError("beta must be [B, T, H]")
-    if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda):
-        raise ValueError("cu_seqlens must be an int32 device tensor")
+    if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1
+                                   or cu_seqlens.numel() < 1 or not cu_seqlens.is_contiguous()
+                                   or cu_seqlens.device != dev):
+        raise ValueError("cu_seqlens must be a contiguous int32 [N + 1] tensor on q's device")
+    if cu_seqlens is not None and q.shape[0] != 1:
+        raise ValueError("with cu_seqlens the batch dimension must be 1 (sequences packed into one row)")
+
+
+def _check_state(name, t, shape, device):
+    """A state tensor the kernels read or write: contiguous fp32 of `shape` on `device`."""
+    if t is None:
+        return
+    if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != tuple(shape) or t.device != device:
+        raise ValueError(f"{name} must be a contiguous float32 {list(shape)} tensor on q's device")
+
+
+def _check_out(name, t, shape, device):
+    """An output the kernels write: contiguous fp32 of `shape` on `device`."""
+    if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != tuple(shape) or t.device != device:
+        raise ValueError(f"{name} must be a contiguous float32 {list(shape)} tensor on q's device")
 
 
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
@@ -76,6 +98,13 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
         raise ValueError(f"kernel must be one of {sorted(KERNELS)}")
     return _forward("kda_fwd_kernel", q, k, v, g, beta, cu_seqlens, initial_state, output_final_state,
                     out, final_state, stream, ctypes.c_int32(KERNELS[kernel]), workspace=workspace)
+
+
+def fwd_workspace_size(q: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None) -> int:
+    """Bytes of device workspace fwd() / gdn_fwd() use for inputs shaped like q
+    (kda_fwd_workspace_size; 0 for most shapes). Passing a workspace of at least
+    this size to fwd() keeps it from allocating."""
+    return int(lib().kda_fwd_workspace_size(ctypes.byref(_desc(q, cu_seqlens))))
 
 
 def kernel_workspace_size(q: torch.Tensor, kernel: str, cu_seqlens: Optional[torch.Tensor] = None) -> int:
@@ -104,15 +133,16 @@ def _forward(entry, q, k, v, g, beta, cu_seqlens, initial_state, output_final_st
         d.workspace = workspace.data_ptr()
         d.workspace_bytes = workspace.numel() * workspace.element_size()
     B, T, H, _ = q.shape
-    if initial_state is not None:
-        if initial_state.dtype != torch.float32 or not initial_state.is_contiguous() \
-                or tuple(initial_state.shape) != (d.num_seqs, H, D, D):
-            raise ValueError("initial_state must be a contiguous float32 [N, H, 128, 128] tensor")
+    sshape = (d.num_seqs, H, D, D)
+    _check_state("initial_state", initial_state, sshape, q.device)
+    if out is not None:
+        _check_out("out", out, (B, T, H, D), q.device)
+    if final_state is not None:
+        _check_out("final_state", final_state, sshape, q.device)
     o = out if out is not None else torch.empty((B, T, H, D), dtype=torch.float32, device=q.device)
     hT = None
     if output_final_state:
-        hT = final_state if final_state is not None else torch.empty(
-            (d.num_seqs, H, D, D), dtype=torch.float32, device=q.device)
+        hT = final_state if final_state is not None else torch.empty(sshape, dtype=torch.float32, device=q.device)
     s = (stream or torch.cuda.current_stream(q.device)).cuda_stream
     rc = getattr(lib(), entry)(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
                                _ptr(initial_state), _ptr(o), _ptr(hT), ctypes.byref(d), *extra,
@@ -133,9 +163,11 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
     N, T, H, _ = q.shape
     if T != 1:
         raise ValueError("decode_step takes one token per sequence ([N, 1, H, 128])")
-    if state is not None and (state.dtype != torch.float32 or not state.is_contiguous()
-                              or tuple(state.shape) != (N, H, D, D)):
-        raise ValueError("state must be a contiguous float32 [N, H, 128, 128] tensor")
+    _check_state("state", state, (N, H, D, D), q.device)
+    if out is not None:
+        _check_out("out", out, (N, 1, H, D), q.device)
+    if new_state is not None:
+        _check_out("new_state", new_state, (N, H, D, D), q.device)
     if in_place:
         if state is None:
             raise ValueError("in_place needs a state")

@@ -15,9 +15,9 @@ STATUS = {0: "KDA_OK", -1: "KDA_ERR_NULL", -2: "KDA_ERR_SHAPE", -3: "KDA_ERR_UNS
 
 # every symbol include/kda.h declares
 EXPORTS = ["kda_status_string", "kda_version", "kda_fwd_check", "kda_fwd", "kda_gdn_fwd", "kda_fwd_kernel",
-           "kda_fwd_kernel_workspace_size",
+           "kda_fwd_kernel_workspace_size", "kda_fwd_workspace_size",
            "kda_decode_step", "kda_staged_layout",
-           "kda_fwd_workspace_size", "kda_stage_chunk_map", "kda_stage_gate_scan", "kda_stage_intra",
+           "kda_staged_workspace_size", "kda_stage_chunk_map", "kda_stage_gate_scan", "kda_stage_intra",
            "kda_stage_recurrence", "kda_stage_output", "kda_fwd_staged"]
 
 
@@ -68,6 +68,8 @@ def lib():
         L.kda_decode_step.restype = ctypes.c_int
         L.kda_fwd_workspace_size.argtypes = [ctypes.POINTER(Desc)]
         L.kda_fwd_workspace_size.restype = ctypes.c_size_t
+        L.kda_staged_workspace_size.argtypes = [ctypes.POINTER(Desc)]
+        L.kda_staged_workspace_size.restype = ctypes.c_size_t
         L.kda_staged_layout.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Layout)]
         L.kda_staged_layout.restype = ctypes.c_int
         D = ctypes.POINTER(Desc)

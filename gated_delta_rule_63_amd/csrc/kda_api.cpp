@@ -15,6 +15,15 @@ namespace {
 
 constexpr int32_t kVersion = 100;  // 0.1.0
 
+// Size limits, so that no index or byte count below overflows: at most 2^46
+// elements per [B, T, H, 128] tensor and fewer than 2^27 (sequence, head)
+// chains. Tested without overflowing (each factor is below 2^31).
+bool sizes_ok(const kda_desc_t* d) {
+    const long long tok = (long long)d->B * d->T;   // < 2^62
+    if (tok > (((long long)1 << 46) / 128) / d->H) return false;
+    return (long long)d->num_seqs * d->H <= INT_MAX / 16;
+}
+
 kda_status_t check(const void* q, const void* k, const void* v, const float* g, const float* beta,
                    const int32_t* cu_seqlens, const void* o, const kda_desc_t* d) {
     if (!d) return KDA_ERR_NULL;
@@ -28,9 +37,8 @@ kda_status_t check(const void* q, const void* k, const void* v, const float* g, 
     } else if (d->num_seqs != d->B) {
         return KDA_ERR_SHAPE;
     }
+    if (!sizes_ok(d)) return KDA_ERR_SHAPE;
     const long long tok = (long long)d->B * d->T;
-    if (tok * d->H * 128 > (long long)1 << 46) return KDA_ERR_SHAPE;
-    if ((long long)d->num_seqs * d->H > INT_MAX / 16) return KDA_ERR_SHAPE;
     if (tok > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL;
     return KDA_OK;
 }
@@ -44,6 +52,7 @@ kda_status_t check_desc(const kda_desc_t* d, bool varlen) {
     if (d->out_dtype != KDA_BF16 && d->out_dtype != KDA_F32) return KDA_ERR_DTYPE;
     if (d->out_dtype != KDA_F32) return KDA_ERR_UNSUPPORTED;
     if (varlen ? (d->B != 1 || d->num_seqs < 0) : (d->num_seqs != d->B)) return KDA_ERR_SHAPE;
+    if (!sizes_ok(d)) return KDA_ERR_SHAPE;
     return KDA_OK;
 }
 
@@ -99,13 +108,16 @@ constexpr int kMinSlice = 4096;   // tokens per slice before a chain is cut into
 // a combine kernel forms slice 2's start state; pass 2 reruns slice 1 and runs
 // slice 2 from their true start states. The critical path shrinks to two
 // thirds at the price of one extra slice of work per chain.
-bool use_slices(const kda::FwdArgs& a, const kda_desc_t* d, bool varlen, int cus) {
-    return d->in_dtype == KDA_BF16 && !varlen && d->T >= 3 * kMinSlice && 6LL * a.nchains <= cus;
+bool use_slices(long long nchains, const kda_desc_t* d, bool varlen, int cus) {
+    return d->in_dtype == KDA_BF16 && !varlen && d->T >= 3 * kMinSlice && 6LL * nchains <= cus;
 }
+
+// Workspace of the slice route: four fp32 states per chain (S1, R1, Pmap1, S2).
+size_t slice_workspace_bytes(long long nchains) { return (size_t)nchains * 4 * 128 * 128 * sizeof(float); }
 
 hipError_t run_slices(const kda::FwdArgs& a, const kda_desc_t* d, int cus, hipStream_t s) {
     const size_t per = (size_t)a.nchains * 128 * 128;
-    const size_t bytes = 4 * per * sizeof(float);
+    const size_t bytes = slice_workspace_bytes(a.nchains);
     void* ws = nullptr;
     bool owned = false;
     if (d->workspace && d->workspace_bytes >= bytes) {
@@ -179,7 +191,7 @@ kda_status_t run_fwd(const kda::FwdArgs& a, const kda_desc_t* desc, const void* 
     const int cus = device_cus();
     if (desc->T == 1 && !varlen && aligned16(o) && aligned16(h0) && aligned16(hT))
         e = kda::launch_decode(a, f32, s);   // one token per sequence: a single recurrence step
-    else if (use_slices(a, desc, varlen, cus))
+    else if (use_slices(a.nchains, desc, varlen, cus))
         e = run_slices(a, desc, cus, s);
     else
         e = f32 ? kda::launch_fwd_serial(a, true, s) : kda::launch_fwd_pipe(a, cus, s);
@@ -318,7 +330,7 @@ kda_status_t kda_fwd_kernel(const void* q, const void* k, const void* v, const f
 size_t kda_fwd_kernel_workspace_size(const kda_desc_t* desc, int32_t kernel) {
     if (!desc || kernel != KDA_KERNEL_TWO_PASS) return 0;
     if (check_desc(desc, desc->num_seqs != desc->B) != KDA_OK) return 0;
-    return kda::two_pass_workspace(desc->num_seqs * desc->H, desc->T);
+    return kda::two_pass_workspace(desc->num_seqs * desc->H, desc->T);   // sizes checked above
 }
 
 kda_status_t kda_decode_step(const void* q, const void* k, const void* v, const float* g,
@@ -339,9 +351,23 @@ kda_status_t kda_staged_layout(const kda_desc_t* desc, kda_staged_layout_t* out)
     return layout(desc, out);
 }
 
-size_t kda_fwd_workspace_size(const kda_desc_t* desc) {
+size_t kda_staged_workspace_size(const kda_desc_t* desc) {
     kda_staged_layout_t L;
     return layout(desc, &L) == KDA_OK ? L.total : 0;
+}
+
+size_t kda_fwd_workspace_size(const kda_desc_t* desc) {
+    if (!desc) return 0;
+    // shape validation only: stand-in pointers, never dereferenced
+    static const float dummy = 0.f;
+    const float* p = &dummy;
+    // without cu_seqlens num_seqs == B; only then can the slice route run
+    const bool maybe_fixed = desc->num_seqs == desc->B;
+    const int32_t* cu = maybe_fixed ? nullptr : reinterpret_cast<const int32_t*>(p);
+    if (check(p, p, p, p, p, cu, p, desc) != KDA_OK) return 0;
+    if (desc->T == 1) return 0;   // the decode route
+    const long long nchains = (long long)desc->num_seqs * desc->H;
+    return maybe_fixed && use_slices(nchains, desc, false, device_cus()) ? slice_workspace_bytes(nchains) : 0;
 }
 
 kda_status_t kda_stage_chunk_map(const int32_t* cu_seqlens, const kda_desc_t* desc, void* stream) {

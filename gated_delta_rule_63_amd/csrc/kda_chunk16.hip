@@ -16,9 +16,11 @@
 //   Delta = T Diag(beta) (V - (K e^{Gamma}) S)
 //   O     = (Q e^{Gamma}) S + tril_0( (Q e^{Gamma - ref}) (K e^{ref - Gamma})^T ) Delta
 //   S    <- Diag(e^{Gamma_last}) S + (K e^{Gamma_last - Gamma})^T Delta
-// (the chunked form of the delta rule with channel-wise decay; donniechu.com
-// page, section on the KDA recurrence, and toolarium.ru page, section "Почему
-// это новость про инфраструктуру").
+// This is the chunked form of the delta rule with channel-wise decay. The
+// pages print no formula: they describe KDA as Gated DeltaNet refined with
+// channel-wise gating (toolarium.ru page, section "Почему это новость про
+// инфраструктуру"), and the chunked algebra above is derived from the
+// recurrence stated in include/kda.h.
 //
 // Products over the 16 tokens (T Delta, M Delta, Kt^T Delta) run on
 // v_mfma_f32_16x16x16_f16, whose B operand (lane l: K-slots 4*(l/16) + j of

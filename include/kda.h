@@ -51,6 +51,24 @@
  * Edge cases. T = 0 or zero-length sequences are allowed: such a sequence has
  * no output rows and hT = h0 (or 0 without h0).
  *
+ * Operand domain. The bf16 kernels round the state S and the gated operands
+ * K*exp(Gamma), Q*exp(Gamma) and K*exp(Gamma_last - Gamma) (Gamma the in-chunk
+ * cumulative gate, so these factors are at most 1 in magnitude) to fp16 for
+ * their matrix products, keep every product's accumulation and the state
+ * itself in fp32, and split the gated key and query factors of the intra-chunk
+ * blocks into two bf16 terms (fp32 range). The results meet the tolerance of
+ * the tests (2e-2 of RMS(o), 1e-2 of RMS(hT)) when
+ *   - every state entry, h0 included, stays below 65504 in magnitude at every
+ *     32-token chunk boundary, and the entries of q and k are below 65504;
+ *   - g lies in [-5, 0] (the factors of a 32-token chunk then stay within
+ *     e^-80 .. e^75); a gate below about -5.4 sustained over 16 tokens
+ *     overflows them to inf/NaN, and g > 0 is a growing state;
+ *   - beta lies in [0, 1] and the keys are L2-normalised per token and head.
+ * The last condition keeps the state bounded: each step (I - beta k k^T)
+ * Diag(exp g) is then a contraction, so an entry of S grows by at most
+ * beta |v| per token and forgets at the gate's rate. The fp32 path (fp32
+ * q, k, v) uses two-term fp16 operands and has the same domain.
+ *
  * Threads. Every entry point is thread-safe; the only global state is a cache
  * of each device's compute-unit count, written atomically.
  */
@@ -81,8 +99,8 @@ typedef struct kda_desc {
     int32_t num_seqs;        /* N: equals B without cu_seqlens; count of sequences with it */
     int32_t in_dtype;        /* kda_dtype_t of q, k, v                                    */
     int32_t out_dtype;       /* kda_dtype_t of o; only KDA_F32 is built                   */
-    void* workspace;         /* device scratch of the staged path (kda_fwd_staged, kda_stage_*) */
-    size_t workspace_bytes;  /* its size; kda_fwd itself needs none                             */
+    void* workspace;         /* optional device scratch; kda_fwd_workspace_size() says how much   */
+    size_t workspace_bytes;  /* kda_fwd needs (often 0), kda_staged_workspace_size() the staged path */
 } kda_desc_t;
 
 /* Text for a status code (static storage, never NULL). */
@@ -110,13 +128,23 @@ kda_status_t kda_fwd_check(const void* q, const void* k, const void* v, const fl
  * from zero and from the identity alongside the first slice, and the later
  * slices then run from their true start states (two passes of a third of the
  * length each, plus one small product). That path needs 256 KiB per
- * (sequence, head) of device memory: desc->workspace when it is at least that
- * large, else a stream-ordered allocation on `stream`, freed on the same
- * stream (if that allocation fails, the chains run whole). Every other case
- * needs no workspace. */
+ * (sequence, head) of device memory: desc->workspace when it is at least
+ * kda_fwd_workspace_size(desc) bytes, else a stream-ordered allocation on
+ * `stream`, freed on the same stream (if that allocation fails, the chains run
+ * whole). Every other case needs no workspace. */
 kda_status_t kda_fwd(const void* q, const void* k, const void* v, const float* g,
                      const float* beta, const int32_t* cu_seqlens, const float* h0,
                      void* o, float* hT, const kda_desc_t* desc, void* stream);
+
+/* Bytes of device workspace kda_fwd (and kda_gdn_fwd) uses for this
+ * descriptor on the current device: 262,144 per (sequence, head) when the
+ * three-slice route for few long chains applies (bf16, T >= 12288, at most one
+ * chain per six compute units of the current device, no cu_seqlens), else 0.
+ * The descriptor does not say whether cu_seqlens will be passed; with B ==
+ * num_seqs == 1 the fixed-length answer is returned, which is never smaller
+ * than what a varlen call needs. 0 also for an invalid descriptor. Host only;
+ * reads the device's compute-unit count once. */
+size_t kda_fwd_workspace_size(const kda_desc_t* desc);
 
 /* ---------------------------------------------------------------------------
  * Gated DeltaNet forward: the same recurrence with one scalar gate per
@@ -237,8 +265,9 @@ typedef struct kda_staged_layout {
 /* Fills *out for this descriptor (host only). */
 kda_status_t kda_staged_layout(const kda_desc_t* desc, kda_staged_layout_t* out);
 
-/* Bytes of workspace the staged path needs for this descriptor (0 on error). */
-size_t kda_fwd_workspace_size(const kda_desc_t* desc);
+/* Bytes of workspace the staged path needs for this descriptor (0 on error):
+ * kda_staged_layout()'s total. */
+size_t kda_staged_workspace_size(const kda_desc_t* desc);
 
 /* a0: chunk map from cu_seqlens (NULL: B rows of T tokens), built on the device. */
 kda_status_t kda_stage_chunk_map(const int32_t* cu_seqlens, const kda_desc_t* desc, void* stream);

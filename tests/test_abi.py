@@ -121,7 +121,26 @@ def test_staged_layout(K):
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     tok = 8192 * 96 * 128 * 4
     assert L.U - L.W >= tok and L.Delta - L.hc >= 257 * 96 * 128 * 128 * 4 and L.total - L.Delta >= tok
-    assert K.lib().kda_fwd_workspace_size(ctypes.byref(d)) == L.total
+    assert K.lib().kda_staged_workspace_size(ctypes.byref(d)) == L.total
     d2 = desc(K, T=100, N=7)       # varlen: ceil(100/32) + 7 slots
     assert K.lib().kda_staged_layout(ctypes.byref(d2), ctypes.byref(L)) == 0 and L.nslots == 4 + 7
-    assert K.lib().kda_fwd_workspace_size(ctypes.byref(desc(K, Kd=64))) == 0
+    assert K.lib().kda_staged_workspace_size(ctypes.byref(desc(K, Kd=64))) == 0
+
+
+def test_fwd_workspace_size(K):
+    """kda_fwd_workspace_size reports what kda_fwd itself uses: nothing for the
+    single fused launch, four 64 KiB fp32 states per (sequence, head) when few
+    long chains take the three-slice route (this machine has no GPU, so the
+    library assumes the MI355X's 256 compute units)."""
+    size = lambda d: K.lib().kda_fwd_workspace_size(ctypes.byref(d))
+    assert size(desc(K, T=8192, H=96)) == 0                          # headline shape: one fused launch
+    assert size(desc(K, T=8192, H=64)) == 0
+    assert size(desc(K, T=8192, N=6, H=96)) == 0                     # varlen: never sliced
+    assert size(desc(K, T=131072, H=32)) == 32 * 4 * 128 * 128 * 4   # 8 MiB
+    assert size(desc(K, T=131072, H=32)) == 8 << 20
+    assert size(desc(K, T=65536, H=32)) == 8 << 20                   # each half of the 2 x 65536 handoff
+    assert size(desc(K, T=12287, H=32)) == 0                         # too short to slice
+    assert size(desc(K, T=131072, H=48)) == 0                        # more than one chain per six CUs
+    assert size(desc(K, T=131072, H=32, in_dt=1)) == 0               # fp32 inputs run whole
+    assert size(desc(K, T=1, B=4, H=32)) == 0                        # decode route
+    assert size(desc(K, Kd=64)) == 0 and K.lib().kda_fwd_workspace_size(None) == 0

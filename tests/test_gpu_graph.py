@@ -70,8 +70,10 @@ def test_prefill_in_a_graph(what, kw, sliced):
     t = to_device(W.make_inputs(cfg, 22), "bf16")
     o = torch.empty((1, cfg.T, cfg.H, 128), dtype=torch.float32, device=t["q"].device)
     hT = torch.empty((1, cfg.H, 128, 128), dtype=torch.float32, device=t["q"].device)
-    # the sliced path's workspace: four 64 KiB states per (sequence, head)
-    ws = torch.empty(4 * cfg.H * 128 * 128 * 4, dtype=torch.uint8, device=t["q"].device) if sliced else None
+    # kda_fwd's own workspace (the sliced path's states), so nothing is allocated while capturing
+    nws = kda.fwd_workspace_size(t["q"])
+    assert (nws > 0) == sliced
+    ws = torch.empty(nws, dtype=torch.uint8, device=t["q"].device) if nws else None
     run = lambda oo, hh: kda.fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], initial_state=t["h0"], out=oo,
                                  final_state=hh, workspace=ws)
     g = capture(lambda: run(o, hT))

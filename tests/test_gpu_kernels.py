@@ -65,10 +65,10 @@ def test_serial_fp32():
     check(W.make_inputs(cfg, 12, dtype="fp32"), "fp32", "serial", "fp32 T=500")
 
 
-def test_chunk16_headline_shape_sampled_heads():
-    """T = 8192, H = 96: every head computed by the 16-token kernel, three compared."""
+def test_chunk16_headline_shape_all_heads():
+    """T = 8192, H = 96 through the 16-token kernel, every head compared with the oracle."""
     cfg = W.CONFIGS["T8192_H96"]
-    check(W.make_inputs(cfg, 0), "bf16", "chunk16", "T=8192 H=96, heads 0,47,95", heads=[0, 47, 95])
+    check(W.make_inputs(cfg, 0), "bf16", "chunk16", "T=8192 H=96, all heads")
 
 
 def test_fp32_rejected_by_bf16_kernels():
