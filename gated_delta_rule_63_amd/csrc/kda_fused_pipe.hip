@@ -32,8 +32,11 @@
 //
 // Precision: the gated factors of A and M are two-term bf16 splits on both
 // sides (three MFMA terms per product, about 16 significant bits, fp32
-// range); the state waves' operands K*gamma, Q*gamma, Kt and the rounded S are
-// single fp16, and beta (V - P) and Delta two-term fp16.
+// range). The products with the state reuse those key and query factors:
+// (K*gamma) S = Ka (Diag(e^Gamma_ref) S), and likewise for Q, with the scaled
+// state split into two bf16 terms as well, so the inter-chunk terms carry the
+// same 16 bits whatever the state's magnitude. Kt is single fp16, beta (V - P)
+// and Delta two-term fp16.
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -98,30 +101,41 @@ __device__ __forceinline__ float swap_pair(float x) {
 
 // Operands of one chunk for the state waves (double-buffered).
 struct alignas(16) Ops {
-    _Float16 Kg[ROWS32];            // K * exp(Gamma); channels permuted in 32-groups; rows at srow()
-    _Float16 Qg[ROWS32];            // Q * exp(Gamma), same layout
     _Float16 KtT[D][TP];            // (K * exp(Gamma_last - Gamma))^T, [channel][kperm(token)]
     _Float16 Tm[C][TP];             // block-diagonal (I + A)^{-1}, [row][kperm(col)]
     _Float16 A10[16][TP];           // A rows 16-31, cols 0-15, [row][kperm(col)]
     _Float16 M[2][C][TP];           // lower gated Q K^T, [hi, lo][row][kperm(col)]
     float Af[2][16][16];            // diagonal blocks A00, A11 in fp32, [row][col]
     float gl[D];                    // exp(Gamma_last), the chunk's decay per channel
+    float c1[D];                    // exp(Gamma_ref), per channel
     float beta[C];
 };
 
 // Gated factors of one chunk, referenced to Gamma at the chunk's token 15
-// (Gamma_ref): the key and query factors of A and M. Rows at srow().
-struct alignas(16) Smem {
-    Ops op[2];
+// (Gamma_ref): the key and query factors of A and M, and (with the state
+// scaled by exp(Gamma_ref)) of the state products. Rows at srow(); the
+// channels of each 32-group sit in kperm() order, the order in which the
+// state's rows feed a product from registers (any order serves A and M).
+// Double-buffered: the state waves read chunk i's while the helpers write
+// chunk i+1's.
+struct alignas(16) Fac {
     __bf16 Kah[ROWS32];             // k * exp(Gamma_r - Gamma_ref) = Kah + Kal
     __bf16 Kal[ROWS32];
-    __bf16 Kbh[ROWS32];             // k * exp(Gamma_ref - Gamma_r) = Kbh + Kbl
-    __bf16 Kbl[ROWS32];
     __bf16 Qah[ROWS32];             // q * exp(Gamma_r - Gamma_ref) = Qah + Qal
     __bf16 Qal[ROWS32];
+    __bf16 Kbh[ROWS32];             // k * exp(Gamma_ref - Gamma_r) = Kbh + Kbl
+    __bf16 Kbl[ROWS32];
+};
+// The part of Fac the state waves read (the two-kernel form carries it in its records).
+constexpr int FAC_STATE_BYTES = 4 * ROWS32 * 2;
+
+struct alignas(16) Smem {
+    Ops op[2];
+    Fac fac[2];
     float2 segsum[NH][8][NSEG];     // per helper wave: segment sums of each channel pair
     int seq;                        // the sequence this workgroup runs (varlen)
 };
+static_assert(sizeof(Smem) <= 160 * 1024, "one workgroup per CU");
 
 // x = hi + lo for a pair of floats: hi is x cut to bf16 (its upper 16 bits, so
 // x - hi is exact), lo is that remainder rounded to bf16; together they carry
@@ -175,7 +189,7 @@ __device__ __forceinline__ void hfetch(HFetch& f, const FwdArgs& a, long long cb
 // A helper lane's gated keys and queries in fp32 and its channels' decay
 // factors, kept in registers from step 1 to step 3.
 struct HStage {
-    float ka[2][SEG], qa[2][SEG], kb[2][SEG];   // k e^(G_r - G_ref), q e^(G_r - G_ref), k e^(G_ref - G_r)
+    float kb[2][SEG];                           // k e^(G_ref - G_r)
     float c1[2], c2[2];                         // e^(G_ref), e^(G_last - G_ref)
 };
 
@@ -190,7 +204,7 @@ struct HStage {
 // pair of tokens in the chunk. wpre holds this lane's weights of S0..S6 in
 // Gamma at its segment start minus Gamma_ref (-1, 0 or +1).
 template <bool SG>
-__device__ __forceinline__ void factors(Smem& sm, Ops& op, HFetch& f, HStage& hs, int hw, int lane,
+__device__ __forceinline__ void factors(Smem& sm, Ops& op, Fac& fc, HFetch& f, HStage& hs, int hw, int lane,
                                         const float (&wpre)[NSEG - 1],
                                         bool fetch_next, const FwdArgs& a, long long nbase, long long nbeta,
                                         uint32_t ts, const HOffs& offs, int nnv) {
@@ -249,11 +263,16 @@ __device__ __forceinline__ void factors(Smem& sm, Ops& op, HFetch& f, HStage& hs
         c2[1] = c2[0];
     }
     if (seg == 0) *reinterpret_cast<float2*>(&op.gl[c0]) = make_float2(c1[0] * c2[0], c1[1] * c2[1]);
+    if (seg == 1) *reinterpret_cast<float2*>(&op.c1[c0]) = make_float2(c1[0], c1[1]);
 
+    // channel position within the factor arrays' rows (kperm order per 32-group;
+    // c0 is even, so the pair stays adjacent)
+    const int cpos = (c0 & ~31) | kperm(c0 & 31);
 #pragma unroll
     for (int t = 0; t < SEG; ++t) {
-        const int so = srow(SEG * seg + t) + c0;
-        float (&ka)[2][SEG] = hs.ka, (&qa)[2][SEG] = hs.qa, (&kb)[2][SEG] = hs.kb;
+        const int so = srow(SEG * seg + t) + cpos;
+        float ka[2][SEG], qa[2][SEG];
+        float (&kb)[2][SEG] = hs.kb;
         float e1s[2], e2s[2];
 #pragma unroll
         for (int ch = 0; ch < NCH; ++ch) {
@@ -275,28 +294,21 @@ __device__ __forceinline__ void factors(Smem& sm, Ops& op, HFetch& f, HStage& hs
         split_bf16x2(ka[0][t], ka[1][t], kah, kal);
         split_bf16x2(kb[0][t], kb[1][t], kbh, kbl);
         split_bf16x2(qa[0][t], qa[1][t], qah, qal);
-        *reinterpret_cast<uint32_t*>(&sm.Kah[so]) = kah;
-        *reinterpret_cast<uint32_t*>(&sm.Kal[so]) = kal;
-        *reinterpret_cast<uint32_t*>(&sm.Kbh[so]) = kbh;
-        *reinterpret_cast<uint32_t*>(&sm.Kbl[so]) = kbl;
-        *reinterpret_cast<uint32_t*>(&sm.Qah[so]) = qah;
-        *reinterpret_cast<uint32_t*>(&sm.Qal[so]) = qal;
+        *reinterpret_cast<uint32_t*>(&fc.Kah[so]) = kah;
+        *reinterpret_cast<uint32_t*>(&fc.Kal[so]) = kal;
+        *reinterpret_cast<uint32_t*>(&fc.Kbh[so]) = kbh;
+        *reinterpret_cast<uint32_t*>(&fc.Kbl[so]) = kbl;
+        *reinterpret_cast<uint32_t*>(&fc.Qah[so]) = qah;
+        *reinterpret_cast<uint32_t*>(&fc.Qal[so]) = qal;
     }
 }
 
-// Helpers, step 3: the state waves' fp16 operands K*gamma, Q*gamma and K~^T
-// of the lane's elements. Needed only from the next chunk on, so this VALU
-// work runs after the mid-chunk barrier, beside the block products.
+// Helpers, step 3: the state waves' fp16 operand K~^T of the lane's elements.
+// Needed only from the next chunk on, so this VALU work runs after the
+// mid-chunk barrier, beside the block products.
 __device__ __forceinline__ void state_operands(Ops& op, const HStage& hs, int hw, int lane) {
     const int cp = lane & 7, seg = lane >> 3;
     const int c0 = 16 * hw + 2 * cp;
-    const int cpos = (c0 & ~31) | kperm(c0 & 31);
-#pragma unroll
-    for (int t = 0; t < SEG; ++t) {
-        const int so = srow(SEG * seg + t) + cpos;
-        *reinterpret_cast<uint32_t*>(&op.Kg[so]) = pack_f16(hs.ka[0][t] * hs.c1[0], hs.ka[1][t] * hs.c1[1]);
-        *reinterpret_cast<uint32_t*>(&op.Qg[so]) = pack_f16(hs.qa[0][t] * hs.c1[0], hs.qa[1][t] * hs.c1[1]);
-    }
     // K~^T: the lane's four tokens are four consecutive kperm positions
     const int tp = kperm(SEG * seg);
 #pragma unroll
@@ -360,7 +372,7 @@ __device__ __forceinline__ void store_tile(_Float16 (*hi)[TP], _Float16 (*lo)[TP
 // A00 and A11 go to the state waves in fp32 (they invert I + A there); A10 and
 // M as fp16 operands. The zero blocks of Tm, A10 and M are written once, at
 // the kernel's start.
-__device__ __forceinline__ void tiles(Smem& sm, Ops& op, const HStage& hs, int hw, int lane) {
+__device__ __forceinline__ void tiles(const Fac& fc, Ops& op, const HStage& hs, int hw, int lane) {
     const int l16 = lane & 15, grp = lane >> 4;
     if (hw <= 2) {
         // A[r][i] = beta_r (Ka_r . Kb_i) = beta_r (Kah Kbh + Kah Kbl + Kal Kbh):
@@ -370,10 +382,10 @@ __device__ __forceinline__ void tiles(Smem& sm, Ops& op, const HStage& hs, int h
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
             const int ko = 32 * kk + 8 * grp;
-            const bf16x8 kah = lds_vec<bf16x8>(&sm.Kah[srow(rb + l16) + ko]);
-            const bf16x8 kal = lds_vec<bf16x8>(&sm.Kal[srow(rb + l16) + ko]);
-            const bf16x8 kbh = lds_vec<bf16x8>(&sm.Kbh[srow(cb + l16) + ko]);
-            const bf16x8 kbl = lds_vec<bf16x8>(&sm.Kbl[srow(cb + l16) + ko]);
+            const bf16x8 kah = lds_vec<bf16x8>(&fc.Kah[srow(rb + l16) + ko]);
+            const bf16x8 kal = lds_vec<bf16x8>(&fc.Kal[srow(rb + l16) + ko]);
+            const bf16x8 kbh = lds_vec<bf16x8>(&fc.Kbh[srow(cb + l16) + ko]);
+            const bf16x8 kbl = lds_vec<bf16x8>(&fc.Kbl[srow(cb + l16) + ko]);
             acc = mfma16(kah, kbh, acc);
             acc1 = mfma16(kah, kbl, acc1);
             acc2 = mfma16(kal, kbh, acc2);
@@ -398,10 +410,10 @@ __device__ __forceinline__ void tiles(Smem& sm, Ops& op, const HStage& hs, int h
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
             const int ko = 32 * kk + 8 * grp;
-            const bf16x8 qh = lds_vec<bf16x8>(&sm.Qah[srow(rb + l16) + ko]);
-            const bf16x8 ql = lds_vec<bf16x8>(&sm.Qal[srow(rb + l16) + ko]);
-            const bf16x8 kh = lds_vec<bf16x8>(&sm.Kbh[srow(cb + l16) + ko]);
-            const bf16x8 kl = lds_vec<bf16x8>(&sm.Kbl[srow(cb + l16) + ko]);
+            const bf16x8 qh = lds_vec<bf16x8>(&fc.Qah[srow(rb + l16) + ko]);
+            const bf16x8 ql = lds_vec<bf16x8>(&fc.Qal[srow(rb + l16) + ko]);
+            const bf16x8 kh = lds_vec<bf16x8>(&fc.Kbh[srow(cb + l16) + ko]);
+            const bf16x8 kl = lds_vec<bf16x8>(&fc.Kbl[srow(cb + l16) + ko]);
             m0 = mfma16(qh, kh, m0);
             m1 = mfma16(qh, kl, m1);
             m2 = mfma16(ql, kh, m2);
@@ -410,6 +422,125 @@ __device__ __forceinline__ void tiles(Smem& sm, Ops& op, const HStage& hs, int h
         store_tile<true>(op.M[0], op.M[1], m0 + (m1 + m2), rb, cb, hw != 4, l16, grp);
     } else {
         state_operands(op, hs, hw, lane);
+    }
+}
+
+// State waves, first step of a chunk: P = (K*gamma) S and O1 = (Q*gamma) S
+// for the wave's 16 columns, as Ka (Diag(e^Gamma_ref) S) and Qa (Diag(e^Gamma_ref) S)
+// with every operand two-term bf16 (three MFMA terms each): the scaled state
+// as a B operand with its rows in kperm order, the factors as A operands.
+// `fc` holds Kah, Kal, Qah, Qal of the chunk (only those members are read).
+template <typename F>
+__device__ __forceinline__ void state_products(const f32x4 (&S)[8], const Ops& op, const F& fc, int l16, int grp,
+                                               f32x4 (&Pt)[2], f32x4 (&Ot)[2]) {
+    bf16x8 SBh[4], SBl[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        // rows 32kk + 4grp + j (slots 0-3) and 32kk + 16 + 4grp + j (slots 4-7)
+        const float4 ca = lds_vec<float4>(&op.c1[32 * kk + 4 * grp]);
+        const float4 cb = lds_vec<float4>(&op.c1[32 * kk + 16 + 4 * grp]);
+        uint32_t h[4], l[4];
+        split_bf16x2(S[2 * kk][0] * ca.x, S[2 * kk][1] * ca.y, h[0], l[0]);
+        split_bf16x2(S[2 * kk][2] * ca.z, S[2 * kk][3] * ca.w, h[1], l[1]);
+        split_bf16x2(S[2 * kk + 1][0] * cb.x, S[2 * kk + 1][1] * cb.y, h[2], l[2]);
+        split_bf16x2(S[2 * kk + 1][2] * cb.z, S[2 * kk + 1][3] * cb.w, h[3], l[3]);
+        SBh[kk] = __builtin_bit_cast(bf16x8, h);
+        SBl[kk] = __builtin_bit_cast(bf16x8, l);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        Pt[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        Ot[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int off = srow(16 * t + l16) + 32 * kk + 8 * grp;
+            const bf16x8 kh = lds_vec<bf16x8>(&fc.Kah[off]), kl = lds_vec<bf16x8>(&fc.Kal[off]);
+            const bf16x8 qh = lds_vec<bf16x8>(&fc.Qah[off]), ql = lds_vec<bf16x8>(&fc.Qal[off]);
+            Pt[t] = mfma16(kh, SBh[kk], Pt[t]);
+            Ot[t] = mfma16(qh, SBh[kk], Ot[t]);
+            Pt[t] = mfma16(kh, SBl[kk], Pt[t]);
+            Ot[t] = mfma16(qh, SBl[kk], Ot[t]);
+            Pt[t] = mfma16(kl, SBh[kk], Pt[t]);
+            Ot[t] = mfma16(ql, SBh[kk], Ot[t]);
+        }
+    }
+}
+
+// State waves, second step of a chunk (after the mid-chunk barrier): the
+// solve Delta = (I + A)^{-1} Diag(beta) (V - P) over the two diagonal blocks,
+// the output O = O1 + M Delta stored through `ro`, and the state update
+// S <- Diag(gamma_last) S + Kt^T Delta. bt0, bt1 (beta) and ah (A10) were read
+// before the barrier; vcur holds V of the wave's column (raw bf16 bits).
+__device__ __forceinline__ void state_finish(f32x4 (&S)[8], const Ops& op, const f32x4 (&Pt)[2], const f32x4 (&Ot)[2],
+                                             const uint32_t (&vcur)[8], const float4& bt0, const float4& bt1,
+                                             const f16x8& ah, __amdgpu_buffer_rsrc_t ro, const uint32_t (&voff)[8],
+                                             int l16, int grp) {
+    const float bts[2][4] = {{bt0.x, bt0.y, bt0.z, bt0.w}, {bt1.x, bt1.y, bt1.z, bt1.w}};
+    float be[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            be[t][j] = bts[t][j] * (__uint_as_float(vcur[4 * t + j] << 16) - Pt[t][j]);
+    // Delta0 = T00 bE0 (two-term fp16 operand; slots of sub-block 1 are zero)
+    uint32_t bh[4] = {0u, 0u, 0u, 0u}, bl[4] = {0u, 0u, 0u, 0u};
+    split_f16x2(be[0][0], be[0][1], bh[0], bl[0]);
+    split_f16x2(be[0][2], be[0][3], bh[1], bl[1]);
+    f32x4 D0 = {0.f, 0.f, 0.f, 0.f};
+    {
+        const f16x8 th = lds_vec<f16x8>(&op.Tm[l16][8 * grp]);
+        D0 = mfma16(th, __builtin_bit_cast(f16x8, bh), D0);
+        D0 = mfma16(th, __builtin_bit_cast(f16x8, bl), D0);
+    }
+    uint32_t dh[4] = {0u, 0u, 0u, 0u}, dl[4] = {0u, 0u, 0u, 0u};
+    split_f16x2(D0[0], D0[1], dh[0], dl[0]);
+    split_f16x2(D0[2], D0[3], dh[1], dl[1]);
+    // Delta1 = T11 (bE1 - A10 Delta0)
+    f32x4 X = {0.f, 0.f, 0.f, 0.f};
+    {
+        X = mfma16(ah, __builtin_bit_cast(f16x8, dh), X);
+        X = mfma16(ah, __builtin_bit_cast(f16x8, dl), X);
+    }
+    bh[0] = bh[1] = bl[0] = bl[1] = 0u;
+    split_f16x2(be[1][0] - X[0], be[1][1] - X[1], bh[2], bl[2]);
+    split_f16x2(be[1][2] - X[2], be[1][3] - X[3], bh[3], bl[3]);
+    f32x4 D1 = {0.f, 0.f, 0.f, 0.f};
+    {
+        const f16x8 th = lds_vec<f16x8>(&op.Tm[16 + l16][8 * grp]);
+        D1 = mfma16(th, __builtin_bit_cast(f16x8, bh), D1);
+        D1 = mfma16(th, __builtin_bit_cast(f16x8, bl), D1);
+    }
+    split_f16x2(D1[0], D1[1], dh[2], dl[2]);
+    split_f16x2(D1[2], D1[3], dh[3], dl[3]);
+    const f16x8 DBh = __builtin_bit_cast(f16x8, dh), DBl = __builtin_bit_cast(f16x8, dl);
+    // O = (Q*gamma) S + M Delta (rows past the chunk's end are dropped)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const f16x8 mh = lds_vec<f16x8>(&op.M[0][16 * t + l16][8 * grp]);
+        const f16x8 ml = lds_vec<f16x8>(&op.M[1][16 * t + l16][8 * grp]);
+        f32x4 acc = Ot[t];
+        acc = mfma16(mh, DBh, acc);
+        acc = mfma16(mh, DBl, acc);
+        acc = mfma16(ml, DBh, acc);
+        const float ov[4] = {acc[0], acc[1], acc[2], acc[3]};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ov[j]), ro, 2u * voff[4 * t + j], 0, 0);
+    }
+    // S <- Diag(gamma_last) S + Kt^T Delta (single fp16 Kt, two-term Delta)
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const float4 g4 = lds_vec<float4>(&op.gl[16 * m + 4 * grp]);
+        S[m][0] *= g4.x;
+        S[m][1] *= g4.y;
+        S[m][2] *= g4.z;
+        S[m][3] *= g4.w;
+        const f16x8 kt = lds_vec<f16x8>(&op.KtT[16 * m + l16][8 * grp]);
+        S[m] = mfma16(kt, DBh, S[m]);
+        S[m] = mfma16(kt, DBl, S[m]);
     }
 }
 
@@ -579,101 +710,18 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
             } else if (wave < 2) {
                 invert_block(opw, wave, l16, grp);
             }
-            // the state as a B operand: rows in kperm order, rounded to fp16
-            f16x8 SBh[4];
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                uint32_t w[4];
-                w[0] = pack_f16(S[2 * kk][0], S[2 * kk][1]);
-                w[1] = pack_f16(S[2 * kk][2], S[2 * kk][3]);
-                w[2] = pack_f16(S[2 * kk + 1][0], S[2 * kk + 1][1]);
-                w[3] = pack_f16(S[2 * kk + 1][2], S[2 * kk + 1][3]);
-                SBh[kk] = __builtin_bit_cast(f16x8, w);
-            }
             f32x4 Pt[2], Ot[2];
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                Pt[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-                Ot[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const int off = srow(16 * t + l16) + 32 * kk + 8 * grp;
-                    Pt[t] = mfma16(lds_vec<f16x8>(&op.Kg[off]), SBh[kk], Pt[t]);
-                    Ot[t] = mfma16(lds_vec<f16x8>(&op.Qg[off]), SBh[kk], Ot[t]);
-                }
-            }
+            state_products(S, op, sm.fac[ci & 1], l16, grp, Pt, Ot);
             // beta and A10 of this chunk were written before the last barrier:
             // read them now, so the solve after the barrier starts without an
             // LDS round trip (T is written in this phase and is read after it).
             const float4 bt0 = lds_vec<float4>(&op.beta[4 * grp]), bt1 = lds_vec<float4>(&op.beta[16 + 4 * grp]);
             const f16x8 ah = lds_vec<f16x8>(&op.A10[l16][8 * grp]);
             __syncthreads();   // mid-chunk: the helpers' factors of chunk ci+1 are written
-            const float bts[2][4] = {{bt0.x, bt0.y, bt0.z, bt0.w}, {bt1.x, bt1.y, bt1.z, bt1.w}};
-            float be[2][4];
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    be[t][j] = bts[t][j] * (__uint_as_float(vcur[4 * t + j] << 16) - Pt[t][j]);
-            // Delta0 = T00 bE0 (two-term fp16 operand; slots of sub-block 1 are zero)
-            uint32_t bh[4] = {0u, 0u, 0u, 0u}, bl[4] = {0u, 0u, 0u, 0u};
-            split_f16x2(be[0][0], be[0][1], bh[0], bl[0]);
-            split_f16x2(be[0][2], be[0][3], bh[1], bl[1]);
-            f32x4 D0 = {0.f, 0.f, 0.f, 0.f};
-            {
-                const f16x8 th = lds_vec<f16x8>(&op.Tm[l16][8 * grp]);
-                D0 = mfma16(th, __builtin_bit_cast(f16x8, bh), D0);
-                D0 = mfma16(th, __builtin_bit_cast(f16x8, bl), D0);
-            }
-            uint32_t dh[4] = {0u, 0u, 0u, 0u}, dl[4] = {0u, 0u, 0u, 0u};
-            split_f16x2(D0[0], D0[1], dh[0], dl[0]);
-            split_f16x2(D0[2], D0[3], dh[1], dl[1]);
-            // Delta1 = T11 (bE1 - A10 Delta0)
-            f32x4 X = {0.f, 0.f, 0.f, 0.f};
-            {
-                X = mfma16(ah, __builtin_bit_cast(f16x8, dh), X);
-                X = mfma16(ah, __builtin_bit_cast(f16x8, dl), X);
-            }
-            bh[0] = bh[1] = bl[0] = bl[1] = 0u;
-            split_f16x2(be[1][0] - X[0], be[1][1] - X[1], bh[2], bl[2]);
-            split_f16x2(be[1][2] - X[2], be[1][3] - X[3], bh[3], bl[3]);
-            f32x4 D1 = {0.f, 0.f, 0.f, 0.f};
-            {
-                const f16x8 th = lds_vec<f16x8>(&op.Tm[16 + l16][8 * grp]);
-                D1 = mfma16(th, __builtin_bit_cast(f16x8, bh), D1);
-                D1 = mfma16(th, __builtin_bit_cast(f16x8, bl), D1);
-            }
-            split_f16x2(D1[0], D1[1], dh[2], dl[2]);
-            split_f16x2(D1[2], D1[3], dh[3], dl[3]);
-            const f16x8 DBh = __builtin_bit_cast(f16x8, dh), DBl = __builtin_bit_cast(f16x8, dl);
-            // O = (Q*gamma) S + M Delta (rows past the chunk's end are dropped)
-            // an empty resource drops the stores (a slice run for its state only)
+            // O's rows past the chunk's end are dropped; an empty resource drops
+            // every store (a slice run for its state only)
             const auto ro = chunk_rsrc(a.o, base + (long long)cs * ts, 4, (tflags & TASK_NO_OUTPUT) ? 0 : nv, ts, D);
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const f16x8 mh = lds_vec<f16x8>(&op.M[0][16 * t + l16][8 * grp]);
-                const f16x8 ml = lds_vec<f16x8>(&op.M[1][16 * t + l16][8 * grp]);
-                f32x4 acc = Ot[t];
-                acc = mfma16(mh, DBh, acc);
-                acc = mfma16(mh, DBl, acc);
-                acc = mfma16(ml, DBh, acc);
-                const float ov[4] = {acc[0], acc[1], acc[2], acc[3]};
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ov[j]), ro, 2u * voff[4 * t + j], 0, 0);
-            }
-            // S <- Diag(gamma_last) S + Kt^T Delta (single fp16 Kt, two-term Delta)
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const float4 g4 = lds_vec<float4>(&op.gl[16 * m + 4 * grp]);
-                S[m][0] *= g4.x;
-                S[m][1] *= g4.y;
-                S[m][2] *= g4.z;
-                S[m][3] *= g4.w;
-                const f16x8 kt = lds_vec<f16x8>(&op.KtT[16 * m + l16][8 * grp]);
-                S[m] = mfma16(kt, DBh, S[m]);
-                S[m] = mfma16(kt, DBl, S[m]);
-            }
+            state_finish(S, op, Pt, Ot, vcur, bt0, bt1, ah, ro, voff, l16, grp);
 #pragma unroll
             for (int j = 0; j < 8; ++j) vcur[j] = vnxt[j];
             __syncthreads();
@@ -703,22 +751,22 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
         offs.b = (uint32_t)(SEG * seg + (cp & 3)) * (uint32_t)a.H * 4u;
         HFetch f;
         HStage hs;
-        auto prepare = [&](Ops& op, int cs) {
+        auto prepare = [&](int buf, int cs) {
             const bool more = cs + C < t1;
             const int nnv = more ? min(C, t1 - cs - C) : 0;
-            factors<SG>(sm, op, f, hs, hw, lane, wpre, more, a, base + (long long)(cs + C) * ts,
-                    bbase + (long long)(cs + C) * a.H, ts, offs, nnv);
+            factors<SG>(sm, sm.op[buf], sm.fac[buf], f, hs, hw, lane, wpre, more, a, base + (long long)(cs + C) * ts,
+                        bbase + (long long)(cs + C) * a.H, ts, offs, nnv);
             __syncthreads();   // mid-chunk barrier
-            tiles(sm, op, hs, hw, lane);
+            tiles(sm.fac[buf], sm.op[buf], hs, hw, lane);
         };
         if (nch > 0) {
             hfetch<SG>(f, a, base + (long long)t0 * ts, bbase + (long long)t0 * a.H, ts, min(C, t1 - t0), offs);
-            prepare(sm.op[0], t0);
+            prepare(0, t0);
         }
         __syncthreads();
         for (int ci = 0; ci < nch; ++ci) {
             // registers of chunk ci+1 were fetched during the previous prepare()
-            if (ci + 1 < nch) prepare(sm.op[(ci + 1) & 1], t0 + (ci + 1) * C);
+            if (ci + 1 < nch) prepare((ci + 1) & 1, t0 + (ci + 1) * C);
             else __syncthreads();   // the mid-chunk barrier of the last chunk
             __syncthreads();
         }
@@ -734,8 +782,14 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
 // for value; only the place where the operands wait between the halves moves
 // from LDS to HBM (1.28 KB more traffic per token-head each way).
 
-static_assert(sizeof(Ops) % 16 == 0, "records are copied in 16-byte pieces");
-constexpr int OPS_VEC = (int)(sizeof(Ops) / 16);   // 16-byte pieces per record
+// A record: the chunk's Ops and the four factor arrays of its state products.
+struct alignas(16) RecOps {
+    Ops op;
+    __bf16 Kah[ROWS32], Kal[ROWS32], Qah[ROWS32], Qal[ROWS32];
+};
+static_assert(sizeof(RecOps) == sizeof(Ops) + FAC_STATE_BYTES, "no padding inside a record");
+static_assert(sizeof(Ops) % 16 == 0 && FAC_STATE_BYTES % 16 == 0, "records are copied in 16-byte pieces");
+constexpr int OPS_VEC = (int)(sizeof(RecOps) / 16);   // 16-byte pieces per record
 // Copy waves of the recurrence kernel, and the record layout they move.
 constexpr int NCW = 4;
 constexpr int CG_LANES = 64 * (NCW / 2);                            // lanes of one copy group
@@ -745,7 +799,7 @@ constexpr int CG_REGS = (OPS_VEC + CG_LANES - 1) / CG_LANES;        // 16-byte p
 // and make the compiler wait for it there). The pad is never read.
 constexpr int REC_PIECES = CG_REGS * CG_LANES;
 struct alignas(16) OpsBuf {
-    Ops op;
+    RecOps rec;
     uint4 pad[REC_PIECES - OPS_VEC];
 };
 static_assert(sizeof(OpsBuf) == 16 * REC_PIECES, "one record per operand buffer");
@@ -815,19 +869,23 @@ __global__ __launch_bounds__(64 * NH, 1) void kda_prep_pipe(FwdArgs a, uint4* re
     }
     for (int ci = c_begin; ci < c_end; ++ci) {
         Ops& op = sm.op[ci & 1];
+        Fac& fc = sm.fac[ci & 1];
         const int cs = t0 + ci * C;
         const bool more = ci + 1 < c_end;
         const int nnv = more ? min(C, t1 - cs - C) : 0;
-        factors<false>(sm, op, f, hs, hw, lane, wpre, more, a, base + (long long)(cs + C) * ts,
+        factors<false>(sm, op, fc, f, hs, hw, lane, wpre, more, a, base + (long long)(cs + C) * ts,
                        bbase + (long long)(cs + C) * a.H, ts, offs, nnv);
         __syncthreads();
-        tiles(sm, op, hs, hw, lane);
+        tiles(fc, op, hs, hw, lane);
         __syncthreads();
         if (hw < 2) invert_block(op, hw, l16, grp);
         __syncthreads();
-        const uint4* src = reinterpret_cast<const uint4*>(&op);
+        // the record: Ops, then Kah, Kal, Qah, Qal (the first four arrays of Fac)
+        const uint4* src_op = reinterpret_cast<const uint4*>(&op);
+        const uint4* src_fac = reinterpret_cast<const uint4*>(&fc);
+        constexpr int OP_PIECES = (int)(sizeof(Ops) / 16);
         uint4* dst = rec + ((size_t)chain * nch + ci) * REC_PIECES;
-        for (int i = tid; i < OPS_VEC; i += 64 * NH) dst[i] = src[i];
+        for (int i = tid; i < OPS_VEC; i += 64 * NH) dst[i] = i < OP_PIECES ? src_op[i] : src_fac[i - OP_PIECES];
     }
 }
 
@@ -887,91 +945,14 @@ void kda_recur_pipe(FwdArgs a, const uint4* rec, int nch) {
         for (int ci = 0; ci < nch; ++ci) {
             const int cs = t0 + ci * C;
             const int nv = min(C, t1 - cs);
-            const Ops& op = ops[ci & 1].op;
+            const Ops& op = ops[ci & 1].rec.op;
             if (ci + 1 < nch) vfetch(vnxt, ci + 1);
-            f16x8 SBh[4];
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                uint32_t w[4];
-                w[0] = pack_f16(S[2 * kk][0], S[2 * kk][1]);
-                w[1] = pack_f16(S[2 * kk][2], S[2 * kk][3]);
-                w[2] = pack_f16(S[2 * kk + 1][0], S[2 * kk + 1][1]);
-                w[3] = pack_f16(S[2 * kk + 1][2], S[2 * kk + 1][3]);
-                SBh[kk] = __builtin_bit_cast(f16x8, w);
-            }
             f32x4 Pt[2], Ot[2];
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                Pt[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-                Ot[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const int off = srow(16 * t + l16) + 32 * kk + 8 * grp;
-                    Pt[t] = mfma16(lds_vec<f16x8>(&op.Kg[off]), SBh[kk], Pt[t]);
-                    Ot[t] = mfma16(lds_vec<f16x8>(&op.Qg[off]), SBh[kk], Ot[t]);
-                }
-            }
+            state_products(S, op, ops[ci & 1].rec, l16, grp, Pt, Ot);
             const float4 bt0 = lds_vec<float4>(&op.beta[4 * grp]), bt1 = lds_vec<float4>(&op.beta[16 + 4 * grp]);
             const f16x8 ah = lds_vec<f16x8>(&op.A10[l16][8 * grp]);
-            const float bts[2][4] = {{bt0.x, bt0.y, bt0.z, bt0.w}, {bt1.x, bt1.y, bt1.z, bt1.w}};
-            float be[2][4];
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    be[t][j] = bts[t][j] * (__uint_as_float(vcur[4 * t + j] << 16) - Pt[t][j]);
-            uint32_t bh[4] = {0u, 0u, 0u, 0u}, bl[4] = {0u, 0u, 0u, 0u};
-            split_f16x2(be[0][0], be[0][1], bh[0], bl[0]);
-            split_f16x2(be[0][2], be[0][3], bh[1], bl[1]);
-            f32x4 D0 = {0.f, 0.f, 0.f, 0.f};
-            {
-                const f16x8 th = lds_vec<f16x8>(&op.Tm[l16][8 * grp]);
-                D0 = mfma16(th, __builtin_bit_cast(f16x8, bh), D0);
-                D0 = mfma16(th, __builtin_bit_cast(f16x8, bl), D0);
-            }
-            uint32_t dh[4] = {0u, 0u, 0u, 0u}, dl[4] = {0u, 0u, 0u, 0u};
-            split_f16x2(D0[0], D0[1], dh[0], dl[0]);
-            split_f16x2(D0[2], D0[3], dh[1], dl[1]);
-            f32x4 X = {0.f, 0.f, 0.f, 0.f};
-            X = mfma16(ah, __builtin_bit_cast(f16x8, dh), X);
-            X = mfma16(ah, __builtin_bit_cast(f16x8, dl), X);
-            bh[0] = bh[1] = bl[0] = bl[1] = 0u;
-            split_f16x2(be[1][0] - X[0], be[1][1] - X[1], bh[2], bl[2]);
-            split_f16x2(be[1][2] - X[2], be[1][3] - X[3], bh[3], bl[3]);
-            f32x4 D1 = {0.f, 0.f, 0.f, 0.f};
-            {
-                const f16x8 th = lds_vec<f16x8>(&op.Tm[16 + l16][8 * grp]);
-                D1 = mfma16(th, __builtin_bit_cast(f16x8, bh), D1);
-                D1 = mfma16(th, __builtin_bit_cast(f16x8, bl), D1);
-            }
-            split_f16x2(D1[0], D1[1], dh[2], dl[2]);
-            split_f16x2(D1[2], D1[3], dh[3], dl[3]);
-            const f16x8 DBh = __builtin_bit_cast(f16x8, dh), DBl = __builtin_bit_cast(f16x8, dl);
             const auto ro = chunk_rsrc(a.o, base + (long long)cs * ts, 4, nv, ts, D);
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const f16x8 mh = lds_vec<f16x8>(&op.M[0][16 * t + l16][8 * grp]);
-                const f16x8 ml = lds_vec<f16x8>(&op.M[1][16 * t + l16][8 * grp]);
-                f32x4 acc = Ot[t];
-                acc = mfma16(mh, DBh, acc);
-                acc = mfma16(mh, DBl, acc);
-                acc = mfma16(ml, DBh, acc);
-                const float ov[4] = {acc[0], acc[1], acc[2], acc[3]};
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ov[j]), ro, 2u * voff[4 * t + j], 0, 0);
-            }
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const float4 g4 = lds_vec<float4>(&op.gl[16 * m + 4 * grp]);
-                S[m][0] *= g4.x;
-                S[m][1] *= g4.y;
-                S[m][2] *= g4.z;
-                S[m][3] *= g4.w;
-                const f16x8 kt = lds_vec<f16x8>(&op.KtT[16 * m + l16][8 * grp]);
-                S[m] = mfma16(kt, DBh, S[m]);
-                S[m] = mfma16(kt, DBl, S[m]);
-            }
+            state_finish(S, op, Pt, Ot, vcur, bt0, bt1, ah, ro, voff, l16, grp);
 #pragma unroll
             for (int j = 0; j < 8; ++j) vcur[j] = vnxt[j];
             __syncthreads();   // ops[ci & 1] is free, ops[(ci + 1) & 1] holds record ci+1
@@ -1012,6 +993,7 @@ void kda_recur_pipe(FwdArgs a, const uint4* rec, int nch) {
         }
     }
 }
+
 
 }  // namespace pipe
 
