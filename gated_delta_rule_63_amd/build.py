@@ -14,6 +14,11 @@ HIPCC_FLAGS = [
     "-Wall", "-Wno-unused-function",
     # packed fp32 instructions stay off: the compiler may not form them
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # multiply-adds are fused only where one source expression (or an explicit
+    # fmaf) asks for it: with fusion across statements the choice depends on
+    # the kernel a helper is inlined into, and two kernels running the same
+    # helpers (the fused kernel and its two-kernel form) would round apart
+    "-ffp-contract=on",
 ]
 
 

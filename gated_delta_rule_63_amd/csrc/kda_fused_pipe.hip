@@ -319,14 +319,15 @@ __device__ __forceinline__ void state_operands(Ops& op, const HStage& hs, int hw
     }
 }
 
-// X Y for 16 x 16 fp32 matrices on fp32 MFMA, from X^T and Y in accumulator
-// layout (lane: rows 4grp+j, column l16), into the same layout, added to c.
-// Product m pairs K-slot g with index 4g + m, which is register j = m of both
-// operands.
+// X Y for 16 x 16 matrices, from X^T and Y in accumulator layout (lane: rows
+// 4grp+j, column l16), into the same layout, added to c (fp32). That layout is
+// both the A operand of X (row l16, K-slots 4grp+j) and the B operand of Y
+// (K-slots 4grp+j, column l16) of one 16x16x16 fp16 MFMA: the operands are
+// rounded to fp16, the product accumulates in fp32.
 __device__ __forceinline__ f32x4 mprod(const f32x4& xt, const f32x4& y, f32x4 c) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) c = mfma16x4(xt[m], y[m], c);
-    return c;
+    const f16x4 a = {(_Float16)xt[0], (_Float16)xt[1], (_Float16)xt[2], (_Float16)xt[3]};
+    const f16x4 b = {(_Float16)y[0], (_Float16)y[1], (_Float16)y[2], (_Float16)y[3]};
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 
 // Stores a 16 x 16 accumulator tile (lane: rows 4grp+j, column l16) into a
@@ -366,18 +367,53 @@ __device__ __forceinline__ void store_tile(_Float16 (*hi)[TP], _Float16 (*lo)[TP
     }
 }
 
+// (I + A_bb)^{-1} of one diagonal block, from A_bb in fp32 (op.Af), into Tm as
+// an fp16 operand. (I + A)^{-1} = (I - A)(I + A^2)(I + A^4)(I + A^8): A
+// is strictly lower triangular, so A^16 = 0 and the product is the whole
+// Neumann series (the factors commute). The identity terms stay exact in the
+// fp32 accumulators; only the powers of A pass through fp16 operands. With
+// |A_ri| <= about 1 (unit keys, beta <= 1, decays <= 1) an entry of A^n is at
+// most C(14, n-1), so A^8 stays below 3432, well inside fp16's range.
+__device__ __forceinline__ void invert_block(Ops& op, int b, int l16, int grp) {
+    f32x4 A, At, ImA;
+    const float4 t4 = lds_vec<float4>(&op.Af[b][l16][4 * grp]);   // A^T in accumulator layout
+    At[0] = t4.x; At[1] = t4.y; At[2] = t4.z; At[3] = t4.w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = 4 * grp + j;
+        A[j] = op.Af[b][r][l16];
+        ImA[j] = (l16 == r ? 1.f : 0.f) - A[j];
+    }
+    const f32x4 Z = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 A2 = mprod(At, A, Z), A2t = mprod(A, At, Z);
+    const f32x4 Q1 = mprod(A2t, ImA, ImA);               // (I + A^2)(I - A)
+    const f32x4 A4 = mprod(A2t, A2, Z), A4t = mprod(A2, A2t, Z);
+    const f32x4 Q2 = mprod(A4t, Q1, Q1);                 // (I + A^4) Q1
+    const f32x4 A8t = mprod(A4, A4t, Z);
+    const f32x4 Tb = mprod(A8t, Q2, Q2);                 // (I + A^8) Q2
+    store_tile<false>(op.Tm, nullptr, Tb, 16 * b, 16 * b, false, l16, grp);
+}
+
 // Helpers, step 2: the gated K K^T blocks of A and the gated Q K^T blocks of
 // M, each from two-term bf16 factors (three MFMA terms), fp32 accumulation:
-//   hw 0: A00   hw 1: A11   hw 2: A10   hw 3: M00   hw 4: M10   hw 5: M11
-// A00 and A11 go to the state waves in fp32 (they invert I + A there); A10 and
-// M as fp16 operands. The zero blocks of Tm, A10 and M are written once, at
-// the kernel's start.
+//   hw 0: A00   hw 1: A11   hw 2: A10   hw 3: M00   hw 6: M10   hw 7: M11
+//   (hw 4, 5: only K~^T)
+// so that each SIMD (helper waves hw and hw + 4 share one) carries about the
+// same block work. A00 and A11 go to the state waves in fp32 (they invert
+// I + A there, under the helpers' element work); A10 and M are stored as fp16
+// operands. The zero blocks of Tm, A10 and M are written once, at the kernel's
+// start.
 __device__ __forceinline__ void tiles(const Fac& fc, Ops& op, const HStage& hs, int hw, int lane) {
     const int l16 = lane & 15, grp = lane >> 4;
-    if (hw <= 2) {
+    const int blk = hw < 4 ? hw : (hw >= 6 ? hw - 2 : -1);   // 0 A00, 1 A11, 2 A10, 3 M00, 4 M10, 5 M11
+    if (blk < 0) {
+        state_operands(op, hs, hw, lane);
+        return;
+    }
+    if (blk <= 2) {
         // A[r][i] = beta_r (Ka_r . Kb_i) = beta_r (Kah Kbh + Kah Kbl + Kal Kbh):
         // lane holds column i = l16 of rows r = 4grp + j
-        const int rb = hw == 0 ? 0 : 16, cb = hw == 1 ? 16 : 0;
+        const int rb = blk == 0 ? 0 : 16, cb = blk == 1 ? 16 : 0;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc1 = acc, acc2 = acc;
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
@@ -392,20 +428,20 @@ __device__ __forceinline__ void tiles(const Fac& fc, Ops& op, const HStage& hs, 
         }
         state_operands(op, hs, hw, lane);   // VALU work while the products finish
         acc += acc1 + acc2;
-        if (hw < 2) {
+        if (blk < 2) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 4 * grp + j;
-                op.Af[hw][r][l16] = (l16 < r) ? op.beta[rb + r] * acc[j] : 0.f;
+                op.Af[blk][r][l16] = (l16 < r) ? op.beta[rb + r] * acc[j] : 0.f;
             }
         } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[j] *= op.beta[16 + 4 * grp + j];
             store_tile<false>(op.A10, nullptr, acc, 0, 0, false, l16, grp);
         }
-    } else if (hw <= 5) {
+    } else {
         // M[r][i] = Qa_r . Kb_i (i <= r) = Qah Kbh + Qah Kbl + Qal Kbh
-        const int rb = hw == 3 ? 0 : 16, cb = hw == 5 ? 16 : 0;
+        const int rb = blk == 3 ? 0 : 16, cb = blk == 5 ? 16 : 0;
         f32x4 m0 = {0.f, 0.f, 0.f, 0.f}, m1 = m0, m2 = m0;
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
@@ -419,9 +455,7 @@ __device__ __forceinline__ void tiles(const Fac& fc, Ops& op, const HStage& hs, 
             m2 = mfma16(ql, kh, m2);
         }
         state_operands(op, hs, hw, lane);
-        store_tile<true>(op.M[0], op.M[1], m0 + (m1 + m2), rb, cb, hw != 4, l16, grp);
-    } else {
-        state_operands(op, hs, hw, lane);
+        store_tile<true>(op.M[0], op.M[1], m0 + (m1 + m2), rb, cb, blk != 4, l16, grp);
     }
 }
 
@@ -542,30 +576,6 @@ __device__ __forceinline__ void state_finish(f32x4 (&S)[8], const Ops& op, const
         S[m] = mfma16(kt, DBh, S[m]);
         S[m] = mfma16(kt, DBl, S[m]);
     }
-}
-
-// State waves: (I + A_bb)^{-1} of one diagonal block, from A_bb in fp32, into
-// Tm as an fp16 operand. (I + A)^{-1} = (I - A)(I + A^2)(I + A^4)(I + A^8): A
-// is strictly lower triangular, so A^16 = 0 and the product is the whole
-// Neumann series (the factors commute).
-__device__ __forceinline__ void invert_block(Ops& op, int b, int l16, int grp) {
-    f32x4 A, At, ImA;
-    const float4 t4 = lds_vec<float4>(&op.Af[b][l16][4 * grp]);   // A^T in accumulator layout
-    At[0] = t4.x; At[1] = t4.y; At[2] = t4.z; At[3] = t4.w;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = 4 * grp + j;
-        A[j] = op.Af[b][r][l16];
-        ImA[j] = (l16 == r ? 1.f : 0.f) - A[j];
-    }
-    const f32x4 Z = {0.f, 0.f, 0.f, 0.f};
-    const f32x4 A2 = mprod(At, A, Z), A2t = mprod(A, At, Z);
-    const f32x4 Q1 = mprod(A2t, ImA, ImA);               // (I + A^2)(I - A)
-    const f32x4 A4 = mprod(A2t, A2, Z), A4t = mprod(A2, A2t, Z);
-    const f32x4 Q2 = mprod(A4t, Q1, Q1);                 // (I + A^4) Q1
-    const f32x4 A8t = mprod(A4, A4t, Z);
-    const f32x4 Tb = mprod(A8t, Q2, Q2);                 // (I + A^8) Q2
-    store_tile<false>(op.Tm, nullptr, Tb, 16 * b, 16 * b, false, l16, grp);
 }
 
 template <int NS, bool SG>
@@ -993,6 +1003,7 @@ void kda_recur_pipe(FwdArgs a, const uint4* rec, int nch) {
         }
     }
 }
+
 
 
 }  // namespace pipe
