@@ -16,7 +16,7 @@ import torch
 
 from ._lib import KDA_BF16, KDA_F32, KERNELS, Desc, KDAError, Layout, lib, status_string  # noqa: F401
 
-__all__ = ["fwd", "gdn_fwd", "fwd_workspace_size", "kernel_workspace_size", "decode_step", "fwd_staged", "Staged", "KDAError", "status_string", "version"]
+__all__ = ["fwd", "gdn_fwd", "fwd_noalloc", "noalloc_max_workspace", "fwd_workspace_size", "kernel_workspace_size", "decode_step", "fwd_staged", "Staged", "KDAError", "status_string", "version"]
 
 D = 128
 
@@ -98,6 +98,23 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
         raise ValueError(f"kernel must be one of {sorted(KERNELS)}")
     return _forward("kda_fwd_kernel", q, k, v, g, beta, cu_seqlens, initial_state, output_final_state,
                     out, final_state, stream, ctypes.c_int32(KERNELS[kernel]), workspace=workspace)
+
+
+def fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+                cu_seqlens: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
+                output_final_state: bool = True, out: Optional[torch.Tensor] = None,
+                final_state: Optional[torch.Tensor] = None,
+                stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """kda_fwd_noalloc: fwd() whose workspace is the library's static device array
+    (no device allocation inside the call; pass `out` and `final_state` to keep
+    this wrapper from allocating them). Calls that overlap on one GPU race."""
+    return _forward("kda_fwd_noalloc", q, k, v, g, beta, cu_seqlens, initial_state, output_final_state,
+                    out, final_state, stream)
+
+
+def noalloc_max_workspace() -> int:
+    """Bytes of kda_fwd_noalloc's static workspace."""
+    return int(lib().kda_fwd_noalloc_max_workspace())
 
 
 def fwd_workspace_size(q: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None) -> int:

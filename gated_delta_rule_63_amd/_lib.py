@@ -15,7 +15,8 @@ STATUS = {0: "KDA_OK", -1: "KDA_ERR_NULL", -2: "KDA_ERR_SHAPE", -3: "KDA_ERR_UNS
 
 # every symbol include/kda.h declares
 EXPORTS = ["kda_status_string", "kda_version", "kda_fwd_check", "kda_fwd", "kda_gdn_fwd", "kda_fwd_kernel",
-           "kda_fwd_kernel_workspace_size", "kda_fwd_workspace_size",
+           "kda_fwd_kernel_workspace_size", "kda_fwd_workspace_size", "kda_fwd_noalloc",
+           "kda_fwd_noalloc_max_workspace",
            "kda_decode_step", "kda_staged_layout",
            "kda_staged_workspace_size", "kda_stage_chunk_map", "kda_stage_gate_scan", "kda_stage_intra",
            "kda_stage_recurrence", "kda_stage_output", "kda_fwd_staged"]
@@ -58,6 +59,10 @@ def lib():
         L.kda_fwd_check.restype = ctypes.c_int
         L.kda_fwd.argtypes = [P] * 9 + [ctypes.POINTER(Desc), P]
         L.kda_fwd.restype = ctypes.c_int
+        L.kda_fwd_noalloc.argtypes = [P] * 9 + [ctypes.POINTER(Desc), P]
+        L.kda_fwd_noalloc.restype = ctypes.c_int
+        L.kda_fwd_noalloc_max_workspace.argtypes = []
+        L.kda_fwd_noalloc_max_workspace.restype = ctypes.c_size_t
         L.kda_gdn_fwd.argtypes = [P] * 9 + [ctypes.POINTER(Desc), P]
         L.kda_gdn_fwd.restype = ctypes.c_int
         L.kda_fwd_kernel.argtypes = [P] * 9 + [ctypes.POINTER(Desc), ctypes.c_int32, P]

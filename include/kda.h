@@ -147,6 +147,27 @@ kda_status_t kda_fwd(const void* q, const void* k, const void* v, const float* g
 size_t kda_fwd_workspace_size(const kda_desc_t* desc);
 
 /* ---------------------------------------------------------------------------
+ * kda_fwd for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation. Arguments,
+ * layouts, results and errors as kda_fwd; desc->workspace is ignored. The
+ * workspace kda_fwd would allocate (kda_fwd_workspace_size(desc) bytes, only
+ * for the three-slice route) comes from a static device array of
+ * kda_fwd_noalloc_max_workspace() bytes (8 MiB: 32 sequence-heads on that
+ * route) that each GPU holds from the first call on it until the process ends.
+ * A descriptor that needs more returns KDA_ERR_WORKSPACE before anything is
+ * enqueued. No hipMalloc, hipFree or other allocating call is made.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (on different streams or host threads, or with the array still in use by an
+ * earlier call's kernels on another stream) race and give undefined results.
+ * Calls ordered on one stream are safe. */
+kda_status_t kda_fwd_noalloc(const void* q, const void* k, const void* v, const float* g,
+                             const float* beta, const int32_t* cu_seqlens, const float* h0,
+                             void* o, float* hT, const kda_desc_t* desc, void* stream);
+
+/* Size in bytes of kda_fwd_noalloc's static workspace. */
+size_t kda_fwd_noalloc_max_workspace(void);
+
+/* ---------------------------------------------------------------------------
  * Gated DeltaNet forward: the same recurrence with one scalar gate per
  * (token, head) instead of one per channel. KDA is presented as Gated DeltaNet
  * refined with channel-wise gating, and the pages benchmark FlashKDA against a
