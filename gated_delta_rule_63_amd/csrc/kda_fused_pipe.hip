@@ -57,21 +57,48 @@ struct Split {
 };
 constexpr int SEG = 4;         // tokens per helper lane
 constexpr int NSEG = C / SEG;  // segments per chunk (lanes 8*seg + cp)
-constexpr int LDP = D + 8;     // row pitch of a 2-byte [token][channel] array
-constexpr int SHIFT = 16;      // extra 2-byte elements before each further group of eight rows
-constexpr int TP = C + 8;      // row pitch of a 2-byte [row][32] array
+constexpr int TP = C;          // row length of a 2-byte [row][32] array (unpadded, see tcol)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr int MAX_RANKED = 64;  // varlen batches up to this many sequences run longest first
 static_assert(NH * 16 == D && NSEG * 8 == 64, "helper lanes: 8 channel pairs x 8 segments per wave");
 
-// Row r of a [token][channel] 2-byte array. Each group of eight rows starts 32
-// bytes further on than the plain pitch would put it: the eight segments of a
-// helper wave, which store the same channel pair of eight rows four apart,
-// then fall on four different bank groups (two writes per bank, the least for
-// 256 bytes), while MFMA operand reads of eight consecutive rows stay
-// conflict-free. An array of R rows holds R * LDP + (R / 8 - 1) * SHIFT.
-__device__ __forceinline__ constexpr int srow(int r) { return r * LDP + (r >> 3) * SHIFT; }
-constexpr int ROWS32 = C * LDP + 3 * SHIFT;
+// LDS layouts. A 16-byte LDS read (ds_read_b128) serves a wave in four
+// cycles of sixteen lanes: lanes 0-31, then 32-63, each half split by the
+// parity of lane bits 2-4; the sixteen pieces of one cycle must fall on
+// different 16-byte bank groups of a 256-byte line (64 banks of 4 bytes).
+// 4-byte accesses serve 32 lanes a cycle over 32 banks (a 128-byte line).
+// (Both rules measured on the chip with one access pattern per dispatch and
+// the LDS bank-conflict counter.) An MFMA operand read, lane (row l16,
+// 16-byte piece grp), therefore puts rows 0-3 and 12-15 of one piece in the
+// same cycle as rows 4-11 of the next piece. Rows are unpadded and each
+// row permutes its 16-byte pieces by an XOR, chosen so that those reads and
+// the writers' stores use every bank once per cycle.
+//
+// [token][channel] arrays (128 positions per row): piece q of row r sits at
+// piece q ^ fswz(r), fswz(r) = r0 | r2 << 1 | r3 << 2 | r1 << 3 (bits of r).
+// A helper store instruction (eight channel pairs that fill all four words of
+// two pieces, rows 4s + t for four s) then meets 32 distinct banks, and an
+// operand read of 16 rows meets 16 distinct bank groups in each cycle.
+__device__ __forceinline__ constexpr int fswz(int r) {
+    return (r & 1) | ((r >> 1) & 2) | ((r >> 1) & 4) | ((r << 2) & 8);
+}
+// Element index of (row r, position p) in a [token][channel] array.
+__device__ __forceinline__ constexpr int fidx(int r, int p) {
+    return r * D + ((((p >> 3) ^ fswz(r)) << 3) | (p & 7));
+}
+constexpr int ROWS32 = C * D;
+// Column of (row r, position p) in a [row][32] 2-byte array: the second and
+// third pieces trade places in rows 8-15 of each 16, which makes the 16-row
+// operand reads conflict-free.
+__device__ __forceinline__ constexpr int tcol(int r, int p) {
+    return (((p >> 3) ^ ((r >> 2) & 2)) << 3) | (p & 7);
+}
+// First channel of a helper lane's channel pair: wave hw covers channels
+// 8h .. 8h+7 and 16+8h .. 16+8h+7 of its 32-group (h = hw & 1), whose kperm
+// positions fill two whole 16-byte pieces of a row (see fidx).
+__device__ __forceinline__ constexpr int hchan(int hw, int cp) {
+    return 32 * (hw >> 1) + 8 * (hw & 1) + 2 * (cp & 3) + 16 * (cp >> 2);
+}
 
 // 2^x as one v_exp_f32. Every argument here lies within [-120, 60] (log2
 // units of at most 24 decay steps with g >= -5) or underflows harmlessly:
@@ -113,7 +140,7 @@ struct alignas(16) Ops {
 
 // Gated factors of one chunk, referenced to Gamma at the chunk's token 15
 // (Gamma_ref): the key and query factors of A and M, and (with the state
-// scaled by exp(Gamma_ref)) of the state products. Rows at srow(); the
+// scaled by exp(Gamma_ref)) of the state products. Elements at fidx(); the
 // channels of each 32-group sit in kperm() order, the order in which the
 // state's rows feed a product from registers (any order serves A and M).
 // Double-buffered: the state waves read chunk i's while the helpers write
@@ -132,7 +159,10 @@ constexpr int FAC_STATE_BYTES = 4 * ROWS32 * 2;
 struct alignas(16) Smem {
     Ops op[2];
     Fac fac[2];
-    float2 segsum[NH][8][NSEG];     // per helper wave: segment sums of each channel pair
+    // per helper wave: segment sums of each channel pair, segment s of pair cp
+    // at s ^ (cp & 4), so that the 32 stores of a half-wave and the 16-byte
+    // reads of segment pairs both meet distinct banks
+    float2 segsum[NH][8][NSEG];
     int seq;                        // the sequence this workgroup runs (varlen)
 };
 static_assert(sizeof(Smem) <= 160 * 1024, "one workgroup per CU");
@@ -209,7 +239,7 @@ __device__ __forceinline__ void factors(Smem& sm, Ops& op, Fac& fc, HFetch& f, H
                                         bool fetch_next, const FwdArgs& a, long long nbase, long long nbeta,
                                         uint32_t ts, const HOffs& offs, int nnv) {
     const int cp = lane & 7, seg = lane >> 3;
-    const int c0 = 16 * hw + 2 * cp;
+    const int c0 = hchan(hw, cp);
 
     float L[2][SEG], kv[2][SEG], qv[2][SEG];
     float r0 = 0.f, r1 = 0.f;
@@ -223,7 +253,7 @@ __device__ __forceinline__ void factors(Smem& sm, Ops& op, Fac& fc, HFetch& f, H
         kv[0][t] = k2.x; kv[1][t] = k2.y;
         qv[0][t] = q2.x; qv[1][t] = q2.y;
     }
-    sm.segsum[hw][cp][seg] = make_float2(r0, r1);
+    sm.segsum[hw][cp][seg ^ (cp & 4)] = make_float2(r0, r1);   // see Smem::segsum
     if (hw == 0 && cp < SEG) op.beta[SEG * seg + cp] = f.beta;
     // the fetched registers are consumed: fetch the chunk after this one
     if (fetch_next) hfetch<SG>(f, a, nbase, nbeta, ts, nnv, offs);
@@ -235,7 +265,7 @@ __device__ __forceinline__ void factors(Smem& sm, Ops& op, Fac& fc, HFetch& f, H
     float St[2][NSEG];
 #pragma unroll
     for (int s = 0; s < NSEG; s += 2) {
-        const float4 v = lds_vec<float4>(&sm.segsum[hw][cp][s]);
+        const float4 v = lds_vec<float4>(&sm.segsum[hw][cp][s ^ (cp & 4)]);   // segments s, s + 1
         St[0][s] = v.x; St[1][s] = v.y; St[0][s + 1] = v.z; St[1][s + 1] = v.w;
     }
     float d[2][SEG];
@@ -270,7 +300,7 @@ __device__ __forceinline__ void factors(Smem& sm, Ops& op, Fac& fc, HFetch& f, H
     const int cpos = (c0 & ~31) | kperm(c0 & 31);
 #pragma unroll
     for (int t = 0; t < SEG; ++t) {
-        const int so = srow(SEG * seg + t) + cpos;
+        const int so = fidx(SEG * seg + t, cpos);
         float ka[2][SEG], qa[2][SEG];
         float (&kb)[2][SEG] = hs.kb;
         float e1s[2], e2s[2];
@@ -308,13 +338,13 @@ __device__ __forceinline__ void factors(Smem& sm, Ops& op, Fac& fc, HFetch& f, H
 // mid-chunk barrier, beside the block products.
 __device__ __forceinline__ void state_operands(Ops& op, const HStage& hs, int hw, int lane) {
     const int cp = lane & 7, seg = lane >> 3;
-    const int c0 = 16 * hw + 2 * cp;
+    const int c0 = hchan(hw, cp);
     // K~^T: the lane's four tokens are four consecutive kperm positions
     const int tp = kperm(SEG * seg);
 #pragma unroll
     for (int ch = 0; ch < 2; ++ch) {
         const float c2 = hs.c2[ch];
-        *reinterpret_cast<uint2*>(&op.KtT[c0 + ch][tp]) =
+        *reinterpret_cast<uint2*>(&op.KtT[c0 + ch][tcol(c0 + ch, tp)]) =
             make_uint2(pack_f16(hs.kb[ch][0] * c2, hs.kb[ch][1] * c2), pack_f16(hs.kb[ch][2] * c2, hs.kb[ch][3] * c2));
     }
 }
@@ -359,10 +389,10 @@ __device__ __forceinline__ void store_tile(_Float16 (*hi)[TP], _Float16 (*lo)[TP
         if constexpr (SPLIT) {
             uint32_t wh, wl;
             split_f16x2(x0, x1, wh, wl);
-            *reinterpret_cast<uint32_t*>(&hi[r][cpos]) = wh;
-            *reinterpret_cast<uint32_t*>(&lo[r][cpos]) = wl;
+            *reinterpret_cast<uint32_t*>(&hi[r][tcol(r, cpos)]) = wh;
+            *reinterpret_cast<uint32_t*>(&lo[r][tcol(r, cpos)]) = wl;
         } else {
-            *reinterpret_cast<uint32_t*>(&hi[r][cpos]) = pack_f16(x0, x1);
+            *reinterpret_cast<uint32_t*>(&hi[r][tcol(r, cpos)]) = pack_f16(x0, x1);
         }
     }
 }
@@ -418,10 +448,10 @@ __device__ __forceinline__ void tiles(const Fac& fc, Ops& op, const HStage& hs, 
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
             const int ko = 32 * kk + 8 * grp;
-            const bf16x8 kah = lds_vec<bf16x8>(&fc.Kah[srow(rb + l16) + ko]);
-            const bf16x8 kal = lds_vec<bf16x8>(&fc.Kal[srow(rb + l16) + ko]);
-            const bf16x8 kbh = lds_vec<bf16x8>(&fc.Kbh[srow(cb + l16) + ko]);
-            const bf16x8 kbl = lds_vec<bf16x8>(&fc.Kbl[srow(cb + l16) + ko]);
+            const bf16x8 kah = lds_vec<bf16x8>(&fc.Kah[fidx(rb + l16, ko)]);
+            const bf16x8 kal = lds_vec<bf16x8>(&fc.Kal[fidx(rb + l16, ko)]);
+            const bf16x8 kbh = lds_vec<bf16x8>(&fc.Kbh[fidx(cb + l16, ko)]);
+            const bf16x8 kbl = lds_vec<bf16x8>(&fc.Kbl[fidx(cb + l16, ko)]);
             acc = mfma16(kah, kbh, acc);
             acc1 = mfma16(kah, kbl, acc1);
             acc2 = mfma16(kal, kbh, acc2);
@@ -446,10 +476,10 @@ __device__ __forceinline__ void tiles(const Fac& fc, Ops& op, const HStage& hs, 
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
             const int ko = 32 * kk + 8 * grp;
-            const bf16x8 qh = lds_vec<bf16x8>(&fc.Qah[srow(rb + l16) + ko]);
-            const bf16x8 ql = lds_vec<bf16x8>(&fc.Qal[srow(rb + l16) + ko]);
-            const bf16x8 kh = lds_vec<bf16x8>(&fc.Kbh[srow(cb + l16) + ko]);
-            const bf16x8 kl = lds_vec<bf16x8>(&fc.Kbl[srow(cb + l16) + ko]);
+            const bf16x8 qh = lds_vec<bf16x8>(&fc.Qah[fidx(rb + l16, ko)]);
+            const bf16x8 ql = lds_vec<bf16x8>(&fc.Qal[fidx(rb + l16, ko)]);
+            const bf16x8 kh = lds_vec<bf16x8>(&fc.Kbh[fidx(cb + l16, ko)]);
+            const bf16x8 kl = lds_vec<bf16x8>(&fc.Kbl[fidx(cb + l16, ko)]);
             m0 = mfma16(qh, kh, m0);
             m1 = mfma16(qh, kl, m1);
             m2 = mfma16(ql, kh, m2);
@@ -490,7 +520,7 @@ __device__ __forceinline__ void state_products(const f32x4 (&S)[8], const Ops& o
     for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const int off = srow(16 * t + l16) + 32 * kk + 8 * grp;
+            const int off = fidx(16 * t + l16, 32 * kk + 8 * grp);
             const bf16x8 kh = lds_vec<bf16x8>(&fc.Kah[off]), kl = lds_vec<bf16x8>(&fc.Kal[off]);
             const bf16x8 qh = lds_vec<bf16x8>(&fc.Qah[off]), ql = lds_vec<bf16x8>(&fc.Qal[off]);
             Pt[t] = mfma16(kh, SBh[kk], Pt[t]);
@@ -525,7 +555,7 @@ __device__ __forceinline__ void state_finish(f32x4 (&S)[8], const Ops& op, const
     split_f16x2(be[0][2], be[0][3], bh[1], bl[1]);
     f32x4 D0 = {0.f, 0.f, 0.f, 0.f};
     {
-        const f16x8 th = lds_vec<f16x8>(&op.Tm[l16][8 * grp]);
+        const f16x8 th = lds_vec<f16x8>(&op.Tm[l16][tcol(l16, 8 * grp)]);
         D0 = mfma16(th, __builtin_bit_cast(f16x8, bh), D0);
         D0 = mfma16(th, __builtin_bit_cast(f16x8, bl), D0);
     }
@@ -543,7 +573,7 @@ __device__ __forceinline__ void state_finish(f32x4 (&S)[8], const Ops& op, const
     split_f16x2(be[1][2] - X[2], be[1][3] - X[3], bh[3], bl[3]);
     f32x4 D1 = {0.f, 0.f, 0.f, 0.f};
     {
-        const f16x8 th = lds_vec<f16x8>(&op.Tm[16 + l16][8 * grp]);
+        const f16x8 th = lds_vec<f16x8>(&op.Tm[16 + l16][tcol(l16, 8 * grp)]);
         D1 = mfma16(th, __builtin_bit_cast(f16x8, bh), D1);
         D1 = mfma16(th, __builtin_bit_cast(f16x8, bl), D1);
     }
@@ -553,8 +583,8 @@ __device__ __forceinline__ void state_finish(f32x4 (&S)[8], const Ops& op, const
     // O = (Q*gamma) S + M Delta (rows past the chunk's end are dropped)
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-        const f16x8 mh = lds_vec<f16x8>(&op.M[0][16 * t + l16][8 * grp]);
-        const f16x8 ml = lds_vec<f16x8>(&op.M[1][16 * t + l16][8 * grp]);
+        const f16x8 mh = lds_vec<f16x8>(&op.M[0][16 * t + l16][tcol(l16, 8 * grp)]);
+        const f16x8 ml = lds_vec<f16x8>(&op.M[1][16 * t + l16][tcol(l16, 8 * grp)]);
         f32x4 acc = Ot[t];
         acc = mfma16(mh, DBh, acc);
         acc = mfma16(mh, DBl, acc);
@@ -572,7 +602,7 @@ __device__ __forceinline__ void state_finish(f32x4 (&S)[8], const Ops& op, const
         S[m][1] *= g4.y;
         S[m][2] *= g4.z;
         S[m][3] *= g4.w;
-        const f16x8 kt = lds_vec<f16x8>(&op.KtT[16 * m + l16][8 * grp]);
+        const f16x8 kt = lds_vec<f16x8>(&op.KtT[16 * m + l16][tcol(l16, 8 * grp)]);
         S[m] = mfma16(kt, DBh, S[m]);
         S[m] = mfma16(kt, DBl, S[m]);
     }
@@ -653,11 +683,11 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
         const int bsel = i / (C * 8), r = (i / 8) % C, c = 2 * (i % 8);
         const int col = kperm((r < 16 ? 16 : 0) + c);
         Ops& op = sm.op[bsel];
-        *reinterpret_cast<uint32_t*>(&op.Tm[r][col]) = 0u;
+        *reinterpret_cast<uint32_t*>(&op.Tm[r][tcol(r, col)]) = 0u;
         if (r < 16) {
-            *reinterpret_cast<uint32_t*>(&op.M[0][r][col]) = 0u;
-            *reinterpret_cast<uint32_t*>(&op.M[1][r][col]) = 0u;
-            *reinterpret_cast<uint32_t*>(&op.A10[r][col]) = 0u;
+            *reinterpret_cast<uint32_t*>(&op.M[0][r][tcol(r, col)]) = 0u;
+            *reinterpret_cast<uint32_t*>(&op.M[1][r][tcol(r, col)]) = 0u;
+            *reinterpret_cast<uint32_t*>(&op.A10[r][tcol(r, col)]) = 0u;
         }
     }
     __syncthreads();
@@ -726,7 +756,7 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
             // read them now, so the solve after the barrier starts without an
             // LDS round trip (T is written in this phase and is read after it).
             const float4 bt0 = lds_vec<float4>(&op.beta[4 * grp]), bt1 = lds_vec<float4>(&op.beta[16 + 4 * grp]);
-            const f16x8 ah = lds_vec<f16x8>(&op.A10[l16][8 * grp]);
+            const f16x8 ah = lds_vec<f16x8>(&op.A10[l16][tcol(l16, 8 * grp)]);
             __syncthreads();   // mid-chunk: the helpers' factors of chunk ci+1 are written
             // O's rows past the chunk's end are dropped; an empty resource drops
             // every store (a slice run for its state only)
@@ -746,7 +776,7 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
     } else {
         const int hw = wave - NS;
         const int cp = lane & 7, seg = lane >> 3;
-        const uint32_t coff = 16 * hw + 2 * cp;                        // channel pair offset
+        const uint32_t coff = hchan(hw, cp);                           // channel pair offset
         // weights of the segment sums S0..S6 in Gamma(segment start) - Gamma_ref
         float wpre[NSEG - 1];
 #pragma unroll
@@ -850,15 +880,15 @@ __global__ __launch_bounds__(64 * NH, 1) void kda_prep_pipe(FwdArgs a, uint4* re
         const int bsel = i / (C * 8), r = (i / 8) % C, c = 2 * (i % 8);
         const int col = kperm((r < 16 ? 16 : 0) + c);
         Ops& op = sm.op[bsel];
-        *reinterpret_cast<uint32_t*>(&op.Tm[r][col]) = 0u;
+        *reinterpret_cast<uint32_t*>(&op.Tm[r][tcol(r, col)]) = 0u;
         if (r < 16) {
-            *reinterpret_cast<uint32_t*>(&op.M[0][r][col]) = 0u;
-            *reinterpret_cast<uint32_t*>(&op.M[1][r][col]) = 0u;
-            *reinterpret_cast<uint32_t*>(&op.A10[r][col]) = 0u;
+            *reinterpret_cast<uint32_t*>(&op.M[0][r][tcol(r, col)]) = 0u;
+            *reinterpret_cast<uint32_t*>(&op.M[1][r][tcol(r, col)]) = 0u;
+            *reinterpret_cast<uint32_t*>(&op.A10[r][tcol(r, col)]) = 0u;
         }
     }
     const int cp = lane & 7, seg = lane >> 3;
-    const uint32_t coff = 16 * hw + 2 * cp;
+    const uint32_t coff = hchan(hw, cp);
     float wpre[NSEG - 1];
 #pragma unroll
     for (int s = 0; s < NSEG - 1; ++s)
@@ -960,7 +990,7 @@ void kda_recur_pipe(FwdArgs a, const uint4* rec, int nch) {
             f32x4 Pt[2], Ot[2];
             state_products(S, op, ops[ci & 1].rec, l16, grp, Pt, Ot);
             const float4 bt0 = lds_vec<float4>(&op.beta[4 * grp]), bt1 = lds_vec<float4>(&op.beta[16 + 4 * grp]);
-            const f16x8 ah = lds_vec<f16x8>(&op.A10[l16][8 * grp]);
+            const f16x8 ah = lds_vec<f16x8>(&op.A10[l16][tcol(l16, 8 * grp)]);
             const auto ro = chunk_rsrc(a.o, base + (long long)cs * ts, 4, nv, ts, D);
             state_finish(S, op, Pt, Ot, vcur, bt0, bt1, ah, ro, voff, l16, grp);
 #pragma unroll

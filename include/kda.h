@@ -218,7 +218,7 @@ typedef enum {
 } kda_kernel_t;
 
 /* Bytes of device workspace kda_fwd_kernel needs for `kernel` (0 when it
- * needs none or the descriptor is invalid). TWO_PASS: one 59,392-byte record
+ * needs none or the descriptor is invalid). TWO_PASS: one 53,248-byte record
  * per (sequence, head, 32-token chunk). */
 size_t kda_fwd_kernel_workspace_size(const kda_desc_t* desc, int32_t kernel);
 

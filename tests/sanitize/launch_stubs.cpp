@@ -25,7 +25,7 @@ int pipe_state_waves(int nchains, int cus) { return nchains * 8 <= cus ? 1 : nch
 int pipe_workgroups(int nchains, int state_waves) { return (nchains + 7) / 8 * 8 * (128 / (16 * state_waves)); }
 hipError_t launch_fwd_pipe(const FwdArgs& a, int, hipStream_t) { rec("pipe", &a); return hipSuccess; }
 hipError_t launch_fwd_chunk16(const FwdArgs& a, hipStream_t) { rec("chunk16", &a); return hipSuccess; }
-size_t two_pass_workspace(int nchains, int T) { return (size_t)nchains * ((T + 31) / 32) * 59392; }
+size_t two_pass_workspace(int nchains, int T) { return (size_t)nchains * ((T + 31) / 32) * 53248; }
 hipError_t launch_fwd_two_pass(const FwdArgs& a, void*, int, hipStream_t) { rec("two_pass", &a); return hipSuccess; }
 hipError_t launch_decode(const FwdArgs& a, bool, hipStream_t) { rec("decode", &a); return hipSuccess; }
 hipError_t launch_chunk_map(const StageArgs&, hipStream_t) { rec("stage", nullptr); return hipSuccess; }

@@ -86,9 +86,9 @@ def test_fwd_kernel_rejects_before_launch(K):
     cu = ctypes.c_void_p(0x2000)
     assert L.kda_fwd_kernel(P, P, P, P, P, cu, None, P, None, ctypes.byref(desc(K, N=3)), K.KERNELS["two_pass"],
                             None) == -3                                   # two_pass takes no cu_seqlens
-    # one 59,392-byte operand record per (sequence, head, 32-token chunk)
+    # one 53,248-byte operand record per (sequence, head, 32-token chunk)
     size = lambda d, kern: L.kda_fwd_kernel_workspace_size(ctypes.byref(d), kern)
-    assert size(desc(K, B=2, T=100, H=3), K.KERNELS["two_pass"]) == 2 * 3 * 4 * 59392
+    assert size(desc(K, B=2, T=100, H=3), K.KERNELS["two_pass"]) == 2 * 3 * 4 * 53248
     assert size(desc(K), K.KERNELS["pipe"]) == 0 and size(desc(K, Kd=64), K.KERNELS["two_pass"]) == 0
     assert run(desc(K, in_dt=1), K.KERNELS["pipe"]) == -3
     assert run(desc(K, in_dt=1), K.KERNELS["chunk16"]) == -3
