@@ -93,6 +93,15 @@ constexpr int ROWS32 = C * D;
 __device__ __forceinline__ constexpr int tcol(int r, int p) {
     return (((p >> 3) ^ ((r >> 2) & 2)) << 3) | (p & 7);
 }
+// Column of (row r, position p) in K~^T ([channel][32 tokens]): pieces are
+// permuted by 2 * r2 | r4. Its writers store one 16-byte piece per lane, and
+// 16-byte stores serve eight consecutive lanes a cycle over 32 banks (a
+// 128-byte line; measured like the reads): the eight rows of such a cycle
+// alternate in parity and their four same-parity rows differ in bits 2 and 4.
+// The 16-row operand reads stay conflict-free as well.
+__device__ __forceinline__ constexpr int kcol(int r, int p) {
+    return (((p >> 3) ^ (((r >> 1) & 2) | ((r >> 4) & 1))) << 3) | (p & 7);
+}
 // First channel of a helper lane's channel pair: wave hw covers channels
 // 8h .. 8h+7 and 16+8h .. 16+8h+7 of its 32-group (h = hw & 1), whose kperm
 // positions fill two whole 16-byte pieces of a row (see fidx).
@@ -333,20 +342,38 @@ __device__ __forceinline__ void factors(Smem& sm, Ops& op, Fac& fc, HFetch& f, H
     }
 }
 
+// The value x of lane l ^ 32 (v_permlane32_swap exchanges the upper half of
+// its first operand with the lower half of its second; with both x, the lower
+// lanes find their partners' x in the second result, the upper lanes in the
+// first). No LDS traffic.
+__device__ __forceinline__ uint32_t from_lane_xor32(uint32_t x, int upper) {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return upper ? r[0] : r[1];
+}
+
 // Helpers, step 3: the state waves' fp16 operand K~^T of the lane's elements.
 // Needed only from the next chunk on, so this VALU work runs after the
-// mid-chunk barrier, beside the block products.
+// mid-chunk barrier, beside the block products. Lanes l and l + 32 hold
+// tokens 4s..4s+3 and 16+4s..16+4s+3 of the same two channels, the two halves
+// of one 16-byte kperm piece: they trade one channel's half, and each stores
+// one whole piece (lane l keeps channel cp & 1, lane l + 32 the other).
 __device__ __forceinline__ void state_operands(Ops& op, const HStage& hs, int hw, int lane) {
     const int cp = lane & 7, seg = lane >> 3;
     const int c0 = hchan(hw, cp);
-    // K~^T: the lane's four tokens are four consecutive kperm positions
-    const int tp = kperm(SEG * seg);
+    uint2 pk[2];
 #pragma unroll
     for (int ch = 0; ch < 2; ++ch) {
         const float c2 = hs.c2[ch];
-        *reinterpret_cast<uint2*>(&op.KtT[c0 + ch][tcol(c0 + ch, tp)]) =
-            make_uint2(pack_f16(hs.kb[ch][0] * c2, hs.kb[ch][1] * c2), pack_f16(hs.kb[ch][2] * c2, hs.kb[ch][3] * c2));
+        pk[ch] = make_uint2(pack_f16(hs.kb[ch][0] * c2, hs.kb[ch][1] * c2), pack_f16(hs.kb[ch][2] * c2, hs.kb[ch][3] * c2));
     }
+    const int upper = seg >> 2;                 // lanes 32-63: tokens 16-31
+    const int keep = (cp & 1) ^ upper;          // the channel this lane stores
+    const uint2 send = keep ? pk[0] : pk[1];
+    const uint2 mine = keep ? pk[1] : pk[0];
+    const uint2 got = make_uint2(from_lane_xor32(send.x, upper), from_lane_xor32(send.y, upper));
+    const uint4 piece = upper ? make_uint4(got.x, got.y, mine.x, mine.y) : make_uint4(mine.x, mine.y, got.x, got.y);
+    const int row = c0 + keep;
+    *reinterpret_cast<uint4*>(&op.KtT[row][kcol(row, 8 * (seg & 3))]) = piece;
 }
 
 // X Y for 16 x 16 matrices, from X^T and Y in accumulator layout (lane: rows
@@ -602,7 +629,7 @@ __device__ __forceinline__ void state_finish(f32x4 (&S)[8], const Ops& op, const
         S[m][1] *= g4.y;
         S[m][2] *= g4.z;
         S[m][3] *= g4.w;
-        const f16x8 kt = lds_vec<f16x8>(&op.KtT[16 * m + l16][tcol(l16, 8 * grp)]);
+        const f16x8 kt = lds_vec<f16x8>(&op.KtT[16 * m + l16][kcol(16 * m + l16, 8 * grp)]);
         S[m] = mfma16(kt, DBh, S[m]);
         S[m] = mfma16(kt, DBl, S[m]);
     }
