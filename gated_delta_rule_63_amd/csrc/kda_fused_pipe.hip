@@ -202,6 +202,7 @@ struct HFetch {
 // With a scalar gate (SG) g has beta's layout and gg[t] is token t's offset there.
 struct HOffs {
     uint32_t kq[SEG], gg[SEG], b;
+    bool beta;                      // this wave stores beta (helper wave 0): only it loads it
 };
 
 template <bool SG>
@@ -222,7 +223,31 @@ __device__ __forceinline__ void hfetch(HFetch& f, const FwdArgs& a, long long cb
         f.k[t] = __builtin_amdgcn_raw_buffer_load_b32(rk, off.kq[t], 0, 0);
         f.q[t] = __builtin_amdgcn_raw_buffer_load_b32(rq, off.kq[t], 0, 0);
     }
-    f.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, off.b, 0, 0));
+    if (off.beta) f.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, off.b, 0, 0));
+}
+
+// State waves: the lane's V column vc for a chunk's rows 16 (i >> 2) + 4 grp +
+// (i & 3), i = 0..7, as raw bf16 bits in the low half (zero past the chunk's
+// end). Lanes 2a and 2a + 1 (columns vc, vc + 1) load 4-byte column pairs,
+// the even lane rows i = 0..3 and the odd lane rows i = 4..7: half the load
+// instructions of 2-byte loads. voff2 holds those byte offsets (vpair_offsets);
+// vunpack() trades the partner's half once the loads have landed.
+__device__ __forceinline__ void vpair_offsets(uint32_t (&voff2)[4], int grp, int vc, uint32_t ts) {
+    const int odd = vc & 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) voff2[i] = ((uint32_t)(16 * odd + 4 * grp + i) * ts + (uint32_t)(vc & ~1)) * 2u;
+}
+__device__ __forceinline__ void vload(uint32_t (&raw)[4], __amdgpu_buffer_rsrc_t rv, const uint32_t (&voff2)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) raw[i] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff2[i], 0, 0);
+}
+__device__ __forceinline__ void vunpack(uint32_t (&v)[8], const uint32_t (&raw)[4], int odd) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t p = (uint32_t)__builtin_amdgcn_mov_dpp((int)raw[i], 0xB1, 0xF, 0xF, false);   // lane l ^ 1
+        v[i] = odd ? (p >> 16) : (raw[i] & 0xffffu);
+        v[4 + i] = odd ? (raw[i] >> 16) : (p & 0xffffu);
+    }
 }
 
 // A helper lane's gated keys and queries in fp32 and its channels' decay
@@ -727,16 +752,16 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
         uint32_t voff[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) voff[i] = ((uint32_t)(16 * (i >> 2) + 4 * grp + (i & 3)) * ts + vc) * 2u;
+        uint32_t voff2[4];
+        vpair_offsets(voff2, grp, vc, ts);
         f32x4 S[8];
-        uint32_t vcur[8], vnxt[8];
-        // V of this lane's column for the chunk's tokens 16t + 4grp + j, as raw
-        // bf16 bits (zero past the chunk's end).
-        auto vfetch = [&](uint32_t* dst, int cidx) {
+        uint32_t vcur[8], vraw[4];
+        // V of this lane's column for the chunk's tokens 16t + 4grp + j (see vload)
+        auto vfetch = [&](uint32_t (&dst)[4], int cidx) {
             const int cs = t0 + cidx * C;
             // an empty resource reads zeros (a slice run with v = 0)
             const auto rv = chunk_rsrc(a.v, base + (long long)cs * ts, 2, (tflags & TASK_ZERO_V) ? 0 : min(C, t1 - cs), ts, D);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) dst[i] = __builtin_amdgcn_raw_buffer_load_b16(rv, voff[i], 0, 0);
+            vload(dst, rv, voff2);
         };
 #pragma unroll
         for (int m = 0; m < 8; ++m)
@@ -753,9 +778,8 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
         // there: the state waves issue first when both are ready.
         __builtin_amdgcn_s_setprio(2);
         if (nch > 0) {
-            vfetch(vnxt, 0);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) vcur[j] = vnxt[j];
+            vfetch(vraw, 0);
+            vunpack(vcur, vraw, vc & 1);
             __syncthreads();   // the helpers' mid-chunk barrier of chunk 0
         }
         __syncthreads();
@@ -767,7 +791,7 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
             // V of the next chunk, copied into vcur at the end of this one: the
             // loaded registers never stay pending across the loop edge, so the
             // waits for them are exact and fall after this chunk's work.
-            if (ci + 1 < nch) vfetch(vnxt, ci + 1);
+            if (ci + 1 < nch) vfetch(vraw, ci + 1);
             // (I + A)^{-1} of the two diagonal blocks, from the helpers' A of this
             // chunk, for all state waves after the mid-chunk barrier. It runs on
             // the matrix cores while the helpers' element work runs on the VALUs.
@@ -789,8 +813,7 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
             // every store (a slice run for its state only)
             const auto ro = chunk_rsrc(a.o, base + (long long)cs * ts, 4, (tflags & TASK_NO_OUTPUT) ? 0 : nv, ts, D);
             state_finish(S, op, Pt, Ot, vcur, bt0, bt1, ah, ro, voff, l16, grp);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) vcur[j] = vnxt[j];
+            vunpack(vcur, vraw, vc & 1);
             __syncthreads();
         }
         if (hTp) {
@@ -816,6 +839,7 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
             offs.gg[t] = SG ? (uint32_t)(SEG * seg + t) * (uint32_t)a.H * 4u : 2u * offs.kq[t];
         }
         offs.b = (uint32_t)(SEG * seg + (cp & 3)) * (uint32_t)a.H * 4u;
+        offs.beta = hw == 0;
         HFetch f;
         HStage hs;
         auto prepare = [&](int buf, int cs) {
@@ -927,6 +951,7 @@ __global__ __launch_bounds__(64 * NH, 1) void kda_prep_pipe(FwdArgs a, uint4* re
         offs.gg[t] = 2u * offs.kq[t];
     }
     offs.b = (uint32_t)(SEG * seg + (cp & 3)) * (uint32_t)a.H * 4u;
+    offs.beta = hw == 0;
     HFetch f;
     HStage hs;
     __syncthreads();
@@ -988,13 +1013,14 @@ void kda_recur_pipe(FwdArgs a, const uint4* rec, int nch) {
         uint32_t voff[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) voff[i] = ((uint32_t)(16 * (i >> 2) + 4 * grp + (i & 3)) * ts + vc) * 2u;
+        uint32_t voff2[4];
+        vpair_offsets(voff2, grp, vc, ts);
         f32x4 S[8];
-        uint32_t vcur[8], vnxt[8];
-        auto vfetch = [&](uint32_t* dst, int cidx) {
+        uint32_t vcur[8], vraw[4];
+        auto vfetch = [&](uint32_t (&dst)[4], int cidx) {
             const int cs = t0 + cidx * C;
             const auto rv = chunk_rsrc(a.v, base + (long long)cs * ts, 2, min(C, t1 - cs), ts, D);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) dst[i] = __builtin_amdgcn_raw_buffer_load_b16(rv, voff[i], 0, 0);
+            vload(dst, rv, voff2);
         };
 #pragma unroll
         for (int m = 0; m < 8; ++m)
@@ -1004,24 +1030,22 @@ void kda_recur_pipe(FwdArgs a, const uint4* rec, int nch) {
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __builtin_amdgcn_s_setprio(2);
         if (nch > 0) {
-            vfetch(vnxt, 0);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) vcur[j] = vnxt[j];
+            vfetch(vraw, 0);
+            vunpack(vcur, vraw, vc & 1);
         }
         __syncthreads();   // record 0 is in ops[0]
         for (int ci = 0; ci < nch; ++ci) {
             const int cs = t0 + ci * C;
             const int nv = min(C, t1 - cs);
             const Ops& op = ops[ci & 1].rec.op;
-            if (ci + 1 < nch) vfetch(vnxt, ci + 1);
+            if (ci + 1 < nch) vfetch(vraw, ci + 1);
             f32x4 Pt[2], Ot[2];
             state_products(S, op, ops[ci & 1].rec, l16, grp, Pt, Ot);
             const float4 bt0 = lds_vec<float4>(&op.beta[4 * grp]), bt1 = lds_vec<float4>(&op.beta[16 + 4 * grp]);
             const f16x8 ah = lds_vec<f16x8>(&op.A10[l16][tcol(l16, 8 * grp)]);
             const auto ro = chunk_rsrc(a.o, base + (long long)cs * ts, 4, nv, ts, D);
             state_finish(S, op, Pt, Ot, vcur, bt0, bt1, ah, ro, voff, l16, grp);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) vcur[j] = vnxt[j];
+            vunpack(vcur, vraw, vc & 1);
             __syncthreads();   // ops[ci & 1] is free, ops[(ci + 1) & 1] holds record ci+1
         }
         if (a.hT) {
