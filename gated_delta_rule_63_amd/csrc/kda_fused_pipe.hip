@@ -205,13 +205,27 @@ struct HOffs {
     bool beta;                      // this wave stores beta (helper wave 0): only it loads it
 };
 
+// The fetch is split: k, q and beta (hfetch_kq) early in the element work, g
+// (hfetch_g) at its end. Issuing the scattered loads stalls the issuing wave;
+// the g loads, moved behind the element work, no longer hold up its segment-sum
+// exchange (5% of the chunk period).
 template <bool SG>
-__device__ __forceinline__ void hfetch(HFetch& f, const FwdArgs& a, long long cbase, long long cbeta,
-                                       uint32_t ts, int nv, const HOffs& off) {
+__device__ __forceinline__ void hfetch_kq(HFetch& f, const FwdArgs& a, long long cbase, long long cbeta,
+                                          uint32_t ts, int nv, const HOffs& off) {
     const auto rk = chunk_rsrc(a.k, cbase, 2, nv, ts, D);
     const auto rq = chunk_rsrc(a.q, cbase, 2, nv, ts, D);
-    const auto rg = SG ? chunk_rsrc(a.g, cbeta, 4, nv, (uint32_t)a.H, 1) : chunk_rsrc(a.g, cbase, 4, nv, ts, D);
     const auto rb = chunk_rsrc(a.beta, cbeta, 4, nv, (uint32_t)a.H, 1);
+#pragma unroll
+    for (int t = 0; t < SEG; ++t) {
+        f.k[t] = __builtin_amdgcn_raw_buffer_load_b32(rk, off.kq[t], 0, 0);
+        f.q[t] = __builtin_amdgcn_raw_buffer_load_b32(rq, off.kq[t], 0, 0);
+    }
+    if (off.beta) f.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, off.b, 0, 0));
+}
+template <bool SG>
+__device__ __forceinline__ void hfetch_g(HFetch& f, const FwdArgs& a, long long cbase, long long cbeta,
+                                         uint32_t ts, int nv, const HOffs& off) {
+    const auto rg = SG ? chunk_rsrc(a.g, cbeta, 4, nv, (uint32_t)a.H, 1) : chunk_rsrc(a.g, cbase, 4, nv, ts, D);
 #pragma unroll
     for (int t = 0; t < SEG; ++t) {
         if constexpr (SG) {
@@ -220,10 +234,13 @@ __device__ __forceinline__ void hfetch(HFetch& f, const FwdArgs& a, long long cb
         } else {
             f.g[t] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rg, off.gg[t], 0, 0));
         }
-        f.k[t] = __builtin_amdgcn_raw_buffer_load_b32(rk, off.kq[t], 0, 0);
-        f.q[t] = __builtin_amdgcn_raw_buffer_load_b32(rq, off.kq[t], 0, 0);
     }
-    if (off.beta) f.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, off.b, 0, 0));
+}
+template <bool SG>
+__device__ __forceinline__ void hfetch(HFetch& f, const FwdArgs& a, long long cbase, long long cbeta,
+                                       uint32_t ts, int nv, const HOffs& off) {
+    hfetch_kq<SG>(f, a, cbase, cbeta, ts, nv, off);
+    hfetch_g<SG>(f, a, cbase, cbeta, ts, nv, off);
 }
 
 // State waves: the lane's V column vc for a chunk's rows 16 (i >> 2) + 4 grp +
@@ -289,8 +306,9 @@ __device__ __forceinline__ void factors(Smem& sm, Ops& op, Fac& fc, HFetch& f, H
     }
     sm.segsum[hw][cp][seg ^ (cp & 4)] = make_float2(r0, r1);   // see Smem::segsum
     if (hw == 0 && cp < SEG) op.beta[SEG * seg + cp] = f.beta;
-    // the fetched registers are consumed: fetch the chunk after this one
-    if (fetch_next) hfetch<SG>(f, a, nbase, nbeta, ts, nnv, offs);
+    // k, q and beta are consumed: fetch the chunk after this one (g follows
+    // at the end, see hfetch_kq)
+    if (fetch_next) hfetch_kq<SG>(f, a, nbase, nbeta, ts, nnv, offs);
 
     // all eight segment sums of this channel pair (written by this wave)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -365,6 +383,7 @@ __device__ __forceinline__ void factors(Smem& sm, Ops& op, Fac& fc, HFetch& f, H
         *reinterpret_cast<uint32_t*>(&fc.Qah[so]) = qah;
         *reinterpret_cast<uint32_t*>(&fc.Qal[so]) = qal;
     }
+    if (fetch_next) hfetch_g<SG>(f, a, nbase, nbeta, ts, nnv, offs);
 }
 
 // The value x of lane l ^ 32 (v_permlane32_swap exchanges the upper half of
