@@ -89,6 +89,20 @@ def host_description() -> dict:
             "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}
 
 
+def calib_copy(args):
+    """One device-to-device copy of --calib-copy-mb MiB, so that a counter pass
+    over this run can scale its byte counters by a transfer of known size."""
+    if not args.calib_copy_mb:
+        return
+    import torch
+    nbytes = args.calib_copy_mb << 20
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"[bench] calibration copy of {nbytes} bytes done", file=sys.stderr, flush=True)
+
+
 def bench_decode(args):
     """In-place decode steps: N sequences x 96 heads, one token each per step."""
     import numpy as np
@@ -137,6 +151,7 @@ def bench_decode(args):
     per_head = 3 * 256 + 512 + 4 + 512 + 2 * STATE_BYTES
     bytes_ = N * H * per_head
     achieved = bytes_ / (ms / 1e3) / 1e9
+    calib_copy(args)
     print(json.dumps({
         "metric": f"KDA decode tokens/s (N={N} sequences, H={H}, D=128, bf16, state in place)",
         "value": N / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -184,6 +199,7 @@ def bench_gdn(args):
     per_token_head = 3 * 256 + 4 + 4 + 512          # q, k, v bf16, g and beta fp32, o fp32
     bytes_ = cfg.token_heads * per_token_head + STATE_BYTES * cfg.N * cfg.H * (1 + (1 if cfg.h0 else 0))
     achieved = bytes_ / (ms / 1e3) / 1e9
+    calib_copy(args)
     print(json.dumps({
         "metric": f"Gated DeltaNet prefill tokens/s ({cfg.name}, T={cfg.T}, H={cfg.H}, D=128 bf16)",
         "value": cfg.B * cfg.T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -328,13 +344,7 @@ def main():
             stage_times[name] = entry
         log(f"[bench] stages: {stage_times}")
 
-    if args.calib_copy_mb:
-        nbytes = args.calib_copy_mb << 20
-        src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"[bench] calibration copy of {nbytes} bytes done")
+    calib_copy(args)
 
     tokens = cfg.B * cfg.T
     value = tokens / (ms / 1e3)
