@@ -102,12 +102,14 @@ def test_full_config(name):
 # T = 131072, H = 32 (all heads, and as 2 x 65536 with the state handed over) is in test_gpu_long.py.
 
 
-@pytest.mark.parametrize("gate", ["bj", "mild"])
+@pytest.mark.parametrize("gate", ["bj", "mild", "floor"])
 def test_operand_domain_edge(gate):
-    """Large states and queries: h0 x 100 (entries up to about 50) and q x 8. The
-    kernels round the state, K*gamma, Q*gamma and K~ to fp16 for their products
-    (relative precision 2^-11, finite below 65504), so the error relative to the
-    oracle's RMS must not change with the scale."""
+    """Large states and queries: h0 x 100 (entries up to about 50) and q x 8, with
+    the gate drawn as usual, mild, or at its floor of -5 in every channel and
+    token (in-chunk factors up to e^80 on either side of the reference token).
+    The state products use two-term bf16 factors of the scaled state, and the
+    fp16 operands (T, A10, M, K~, the solve) stay far below 65504, so the error
+    relative to the oracle's RMS must not change with the scale or the gate."""
     cfg = W.variant("T8192_H96", T=1000, H=4, h0=True, gate=gate, name=f"h0 x 100, q x 8, gate={gate}")
     inp = W.make_inputs(cfg, 9)
     inp.h0 *= np.float32(100.0)

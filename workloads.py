@@ -63,7 +63,7 @@ class Config:
     dtype: str = "bf16"         # dtype of q, k, v: "bf16" or "fp32"
     seq_lens: Optional[tuple] = None   # varlen mix (B must be 1); None = fixed length
     h0: bool = False            # draw an initial state per (sequence, head)
-    gate: str = "bj"            # "bj" | "mild" | "zero" | "scalar" | "scalar_mild" (all but "bj" test-only)
+    gate: str = "bj"            # "bj" | "mild" | "zero" | "floor" | "scalar" | "scalar_mild" (all but "bj" test-only)
     beta: str = "bj"            # "bj" | "zero" | "one"
     keys: str = "gauss"         # "gauss" | "onehot" | "same"
     note: str = ""
@@ -170,6 +170,10 @@ def make_inputs(cfg: Config, seed: int, dtype: Optional[str] = None) -> Inputs:
         g = 0.01 * g
     elif cfg.gate == "zero":
         g = np.zeros_like(g)
+    elif cfg.gate == "floor":
+        # every channel at the floor of the draws' range, -5 per token: the
+        # strongest in-chunk decay the generator produces
+        g = np.full_like(g, -5.0)
     g = g.astype(np.float32)
     del gz
 
