@@ -306,6 +306,14 @@ __device__ __forceinline__ void factors(Smem& sm, Ops& op, Fac& fc, HFetch& f, H
     }
     sm.segsum[hw][cp][seg ^ (cp & 4)] = make_float2(r0, r1);   // see Smem::segsum
     if (hw == 0 && cp < SEG) op.beta[SEG * seg + cp] = f.beta;
+    // The fp32 keys and queries are formed before the next chunk's loads are
+    // issued, which frees the fetched registers for them. Left free, the
+    // compiler sinks the conversions into the element loop; the new loads then
+    // land in other registers, copied back at the end of the chunk behind a
+    // wait for every outstanding load, the g prefetch included.
+#pragma unroll
+    for (int t = 0; t < SEG; ++t)
+        asm volatile("" : "+v"(kv[0][t]), "+v"(kv[1][t]), "+v"(qv[0][t]), "+v"(qv[1][t]));
     // k, q and beta are consumed: fetch the chunk after this one (g follows
     // at the end, see hfetch_kq)
     if (fetch_next) hfetch_kq<SG>(f, a, nbase, nbeta, ts, nnv, offs);
@@ -497,20 +505,13 @@ __device__ __forceinline__ void invert_block(Ops& op, int b, int l16, int grp) {
 
 // Helpers, step 2: the gated K K^T blocks of A and the gated Q K^T blocks of
 // M, each from two-term bf16 factors (three MFMA terms), fp32 accumulation:
-//   hw 0: A00   hw 1: A11   hw 2: A10   hw 3: M00   hw 6: M10   hw 7: M11
-//   (hw 4, 5: only K~^T)
-// so that each SIMD (helper waves hw and hw + 4 share one) carries about the
-// same block work. A00 and A11 go to the state waves in fp32 (they invert
-// I + A there, under the helpers' element work); A10 and M are stored as fp16
-// operands. The zero blocks of Tm, A10 and M are written once, at the kernel's
-// start.
-__device__ __forceinline__ void tiles(const Fac& fc, Ops& op, const HStage& hs, int hw, int lane) {
+//   block 0 A00, 1 A11, 2 A10, 3 M00, 4 M10, 5 M11.
+// A00 and A11 go to the state waves in fp32 (they invert I + A there, under
+// the helpers' element work); A10 and M are stored as fp16 operands. The zero
+// blocks of Tm, A10 and M are written once, at the kernel's start. The wave
+// forms its K~^T pieces under the block's products.
+__device__ __forceinline__ void tile_block(const Fac& fc, Ops& op, const HStage& hs, int hw, int lane, int blk) {
     const int l16 = lane & 15, grp = lane >> 4;
-    const int blk = hw < 4 ? hw : (hw >= 6 ? hw - 2 : -1);   // 0 A00, 1 A11, 2 A10, 3 M00, 4 M10, 5 M11
-    if (blk < 0) {
-        state_operands(op, hs, hw, lane);
-        return;
-    }
     if (blk <= 2) {
         // A[r][i] = beta_r (Ka_r . Kb_i) = beta_r (Kah Kbh + Kah Kbl + Kal Kbh):
         // lane holds column i = l16 of rows r = 4grp + j
@@ -558,6 +559,31 @@ __device__ __forceinline__ void tiles(const Fac& fc, Ops& op, const HStage& hs, 
         state_operands(op, hs, hw, lane);
         store_tile<true>(op.M[0], op.M[1], m0 + (m1 + m2), rb, cb, blk != 4, l16, grp);
     }
+}
+
+// The block of helper wave hw with NS state waves (0xFF: none). The waves of
+// a workgroup go to the four SIMDs in turn, so waves w and w + 4 share one
+// (helper hw is wave NS + hw); one block per wave keeps the helpers' second
+// phase short.
+//   NS = 4: every SIMD holds a state wave, and SIMDs 0 and 1 also run the
+//           inverses: one block each there, two each on the other two;
+//   NS = 2: two blocks on each of the two SIMDs without a state wave, one on
+//           each of the others;
+//   NS = 1: one block on each helper wave of the three SIMDs without the state wave.
+// The table's bytes are shifted out with scalar instructions: a table in
+// memory would be a load, and its wait inside the chunk loop would also wait
+// for the input prefetch.
+template <int NS>
+__device__ __forceinline__ int helper_block(int hw) {
+    constexpr uint64_t T = NS == 4 ? 0x0504FFFF03020100ull : (NS == 2 ? 0xFFFF050304020100ull : 0xFF050301FF040200ull);
+    return (int)((T >> (8 * hw)) & 0xFFu);
+}
+
+template <int NS>
+__device__ __forceinline__ void tiles(const Fac& fc, Ops& op, const HStage& hs, int hw, int lane) {
+    const int blk = helper_block<NS>(hw);
+    if (blk == 0xFF) state_operands(op, hs, hw, lane);
+    else tile_block(fc, op, hs, hw, lane, blk);
 }
 
 // State waves, first step of a chunk: P = (K*gamma) S and O1 = (Q*gamma) S
@@ -867,7 +893,7 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
             factors<SG>(sm, sm.op[buf], sm.fac[buf], f, hs, hw, lane, wpre, more, a, base + (long long)(cs + C) * ts,
                         bbase + (long long)(cs + C) * a.H, ts, offs, nnv);
             __syncthreads();   // mid-chunk barrier
-            tiles(sm.fac[buf], sm.op[buf], hs, hw, lane);
+            tiles<NS>(sm.fac[buf], sm.op[buf], hs, hw, lane);
         };
         if (nch > 0) {
             hfetch<SG>(f, a, base + (long long)t0 * ts, bbase + (long long)t0 * a.H, ts, min(C, t1 - t0), offs);
@@ -987,7 +1013,7 @@ __global__ __launch_bounds__(64 * NH, 1) void kda_prep_pipe(FwdArgs a, uint4* re
         factors<false>(sm, op, fc, f, hs, hw, lane, wpre, more, a, base + (long long)(cs + C) * ts,
                        bbase + (long long)(cs + C) * a.H, ts, offs, nnv);
         __syncthreads();
-        tiles(fc, op, hs, hw, lane);
+        tiles<4>(fc, op, hs, hw, lane);   // eight helper waves, two per SIMD
         __syncthreads();
         if (hw < 2) invert_block(op, hw, l16, grp);
         __syncthreads();
