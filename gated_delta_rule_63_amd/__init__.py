@@ -119,8 +119,9 @@ def noalloc_max_workspace() -> int:
 
 def fwd_workspace_size(q: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None) -> int:
     """Bytes of device workspace fwd() / gdn_fwd() use for inputs shaped like q
-    (kda_fwd_workspace_size; 0 for most shapes). Passing a workspace of at least
-    this size to fwd() keeps it from allocating."""
+    (kda_fwd_workspace_size; 0 for most shapes). For few long chains, a workspace
+    of at least this size selects the faster two-slice route and keeps fwd()
+    from allocating; without one, fwd() allocates the three-slice route's."""
     return int(lib().kda_fwd_workspace_size(ctypes.byref(_desc(q, cu_seqlens))))
 
 
@@ -133,11 +134,12 @@ def gdn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, 
             cu_seqlens: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
             output_final_state: bool = True, out: Optional[torch.Tensor] = None,
             final_state: Optional[torch.Tensor] = None,
-            stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+            stream: Optional[torch.cuda.Stream] = None,
+            workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Gated DeltaNet forward (kda_gdn_fwd): as fwd, but g is one fp32 log-decay per
-    (token, head), [B, T, H]."""
+    (token, head), [B, T, H]. workspace: as for fwd (fwd_workspace_size)."""
     return _forward("kda_gdn_fwd", q, k, v, g, beta, cu_seqlens, initial_state, output_final_state,
-                    out, final_state, stream)
+                    out, final_state, stream, workspace=workspace)
 
 
 def _forward(entry, q, k, v, g, beta, cu_seqlens, initial_state, output_final_state, out, final_state,

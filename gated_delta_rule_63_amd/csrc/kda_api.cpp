@@ -102,20 +102,58 @@ kda::FwdArgs fwd_args(const void* q, const void* k, const void* v, const float* 
 constexpr int kMinSlice = 4096;   // tokens per slice before a chain is cut into three
 
 // Few long chains (fixed-length, bf16): the chip holds far more workgroups
-// than the chains fill, and each chain is a long sequential walk. Cut every
-// chain into three slices of whole chunks: pass 1 runs slice 0 for real and,
-// at the same time, slice 1 from zero and from the identity (its affine map);
-// a combine kernel forms slice 2's start state; pass 2 reruns slice 1 and runs
-// slice 2 from their true start states. The critical path shrinks to two
-// thirds at the price of one extra slice of work per chain.
+// than the chains fill, and each chain is a long sequential walk. A slice's
+// state map and its outputs are affine in the state it starts from, so a
+// chain is cut into slices of whole chunks, each later slice run from zero and
+// from the identity alongside the first. Two routes:
+//   two slices (desc->workspace of slice2_workspace_bytes): one pass runs
+//     slice 0 for real and slice 1 from zero (o into o) and from the identity
+//     with v = 0 (its o, ell, into the workspace; its end state is Pmap1);
+//     then hT = Pmap1 S1 + R1, and o of slice 1 += S1^T ell per token. The
+//     critical path is half a chain plus a streaming pass over slice 1's o.
+//   three slices (less workspace, or none: 256 KiB per chain, allocated on
+//     the stream when not given): pass 1 runs slice 0 for real and slice 1
+//     from zero and from the identity; a combine forms slice 2's start state;
+//     pass 2 reruns slice 1 and runs slice 2 from their true start states.
+//     Two thirds of a chain on the critical path.
 bool use_slices(long long nchains, const kda_desc_t* d, bool varlen, int cus) {
     return d->in_dtype == KDA_BF16 && !varlen && d->T >= 3 * kMinSlice && 6LL * nchains <= cus;
 }
 
-// Workspace of the slice route: four fp32 states per chain (S1, R1, Pmap1, S2).
+// Workspace of the three-slice route: four fp32 states per chain (S1, R1, Pmap1, S2).
 size_t slice_workspace_bytes(long long nchains) { return (size_t)nchains * 4 * 128 * 128 * sizeof(float); }
 
+// First token of the two-slice route's second slice.
+int slice2_split(int T) { return (T / 2) / 32 * 32; }
+
+// Workspace of the two-slice route: three fp32 states per chain (S1, R1,
+// Pmap1) and ell, fp32 [B, T - split, H, 128].
+size_t slice2_workspace_bytes(const kda_desc_t* d) {
+    const size_t states = (size_t)d->B * d->H * 3 * 128 * 128 * sizeof(float);
+    return states + (size_t)d->B * (d->T - slice2_split(d->T)) * d->H * 128 * sizeof(float);
+}
+
+hipError_t run_two_slices(const kda::FwdArgs& a, const kda_desc_t* d, int cus, hipStream_t s) {
+    const size_t per = (size_t)a.nchains * 128 * 128;
+    float* S1 = static_cast<float*>(d->workspace);   // state after slice 0
+    float* R1 = S1 + per;                             // slice 1 from zero
+    float* P1 = R1 + per;                             // slice 1's transition map
+    float* ell = P1 + per;                            // slice 1's o from the identity
+    const int T = d->T, s1 = slice2_split(T);
+    kda::FwdArgs p = a;
+    p.ntasks = 3;
+    p.nchains = 3 * a.nchains;
+    p.task[0] = {0, s1, a.h0, S1, 0};
+    p.task[1] = {s1, T, nullptr, R1, 0};
+    p.task[2] = {s1, T, nullptr, P1, kda::TASK_ZERO_V | kda::TASK_IDENTITY_H0, ell, s1, T - s1};
+    hipError_t e = kda::launch_fwd_pipe(p, cus, s);
+    if (e == hipSuccess && a.hT) e = kda::launch_affine_combine(P1, S1, R1, a.hT, a.nchains, s);
+    if (e == hipSuccess) e = kda::launch_state_correction(S1, ell, a.o, a.N, T, a.H, s1, s);
+    return e;
+}
+
 hipError_t run_slices(const kda::FwdArgs& a, const kda_desc_t* d, int cus, hipStream_t s) {
+    if (d->workspace && d->workspace_bytes >= slice2_workspace_bytes(d)) return run_two_slices(a, d, cus, s);
     const size_t per = (size_t)a.nchains * 128 * 128;
     const size_t bytes = slice_workspace_bytes(a.nchains);
     void* ws = nullptr;
@@ -262,6 +300,26 @@ kda_status_t hip_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ER
 
 }  // namespace
 
+namespace kda {
+
+size_t fwd_workspace_bytes(const kda_desc_t* desc, bool smallest) {
+    if (!desc) return 0;
+    // shape validation only: stand-in pointers, never dereferenced
+    static const float dummy = 0.f;
+    const float* p = &dummy;
+    // without cu_seqlens num_seqs == B; only then can the slice routes run
+    const bool maybe_fixed = desc->num_seqs == desc->B;
+    const int32_t* cu = maybe_fixed ? nullptr : reinterpret_cast<const int32_t*>(p);
+    if (check(p, p, p, p, p, cu, p, desc) != KDA_OK) return 0;
+    if (desc->T == 1) return 0;   // the decode route
+    const long long nchains = (long long)desc->num_seqs * desc->H;
+    if (!maybe_fixed || !use_slices(nchains, desc, false, device_cus())) return 0;
+    const size_t two = slice2_workspace_bytes(desc), three = slice_workspace_bytes(nchains);
+    return smallest ? std::min(two, three) : two;
+}
+
+}  // namespace kda
+
 extern "C" {
 
 const char* kda_status_string(kda_status_t s) {
@@ -356,19 +414,7 @@ size_t kda_staged_workspace_size(const kda_desc_t* desc) {
     return layout(desc, &L) == KDA_OK ? L.total : 0;
 }
 
-size_t kda_fwd_workspace_size(const kda_desc_t* desc) {
-    if (!desc) return 0;
-    // shape validation only: stand-in pointers, never dereferenced
-    static const float dummy = 0.f;
-    const float* p = &dummy;
-    // without cu_seqlens num_seqs == B; only then can the slice route run
-    const bool maybe_fixed = desc->num_seqs == desc->B;
-    const int32_t* cu = maybe_fixed ? nullptr : reinterpret_cast<const int32_t*>(p);
-    if (check(p, p, p, p, p, cu, p, desc) != KDA_OK) return 0;
-    if (desc->T == 1) return 0;   // the decode route
-    const long long nchains = (long long)desc->num_seqs * desc->H;
-    return maybe_fixed && use_slices(nchains, desc, false, device_cus()) ? slice_workspace_bytes(nchains) : 0;
-}
+size_t kda_fwd_workspace_size(const kda_desc_t* desc) { return kda::fwd_workspace_bytes(desc, false); }
 
 kda_status_t kda_stage_chunk_map(const int32_t* cu_seqlens, const kda_desc_t* desc, void* stream) {
     if (desc && cu_seqlens == nullptr && desc->num_seqs != desc->B) return KDA_ERR_SHAPE;

@@ -744,6 +744,8 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
     int row, t0, t1;
     const float* h0p = a.h0;
     float* hTp = a.hT;
+    float* outp = a.o;              // o of this workgroup's task, token 0 at token ot0 of the row
+    int ot0 = 0, oT = a.T;
     int tflags = 0;
     if (a.cu) { row = 0; t0 = a.cu[n]; t1 = a.cu[n + 1]; }
     else      { row = n; t0 = 0;       t1 = a.T; }
@@ -763,6 +765,12 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
         };
         h0p = reinterpret_cast<const float*>(uptr(tk.h0));
         hTp = reinterpret_cast<float*>(uptr(tk.hT));
+        float* to = reinterpret_cast<float*>(uptr(tk.o));
+        if (to) {
+            outp = to;
+            ot0 = __builtin_amdgcn_readfirstlane(tk.o_t0);
+            oT = __builtin_amdgcn_readfirstlane(tk.o_T);
+        }
     }
     // uniform per workgroup: keep them scalar (buffer resources are built from them)
     t0 = __builtin_amdgcn_readfirstlane(t0);
@@ -772,6 +780,7 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
     const long long base = (long long)row * a.T * ts + (long long)h * D;
     const long long bbase = (long long)row * a.T * a.H + h;
     const long long sbase = ((long long)n * a.H + h) * D * D;
+    const long long obase = ((long long)row * oT - ot0) * ts + (long long)h * D;   // o of token 0 (from token ot0 on)
 
     // Zero blocks of both operand buffers, never written afterwards: kperm
     // positions 16-31 of rows 0-15 in Tm, M (hi, lo) and A10, and positions
@@ -856,7 +865,7 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
             __syncthreads();   // mid-chunk: the helpers' factors of chunk ci+1 are written
             // O's rows past the chunk's end are dropped; an empty resource drops
             // every store (a slice run for its state only)
-            const auto ro = chunk_rsrc(a.o, base + (long long)cs * ts, 4, (tflags & TASK_NO_OUTPUT) ? 0 : nv, ts, D);
+            const auto ro = chunk_rsrc(outp, obase + (long long)cs * ts, 4, (tflags & TASK_NO_OUTPUT) ? 0 : nv, ts, D);
             state_finish(S, op, Pt, Ot, vcur, bt0, bt1, ah, ro, voff, l16, grp);
             vunpack(vcur, vraw, vc & 1);
             __syncthreads();

@@ -2,9 +2,18 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
+struct kda_desc;
+
 namespace kda {
+
+// Device workspace kda_fwd uses for this descriptor: the two-slice route's
+// (what kda_fwd_workspace_size reports), or with `smallest` the least any
+// route takes without allocating (the three-slice route's when that is
+// smaller). 0 where no route needs any, and for an invalid descriptor.
+size_t fwd_workspace_bytes(const struct kda_desc* desc, bool smallest);
 
 // Arguments of the fused forward kernel. Layouts are those of include/kda.h.
 // One slice of every chain of a fixed-length batch: tokens [t_begin, t_end)
@@ -19,6 +28,10 @@ struct FwdTask {
     const float* h0;        // [N, H, K, V] or nullptr (zero), unless TASK_IDENTITY_H0
     float* hT;              // [N, H, K, V] or nullptr
     int flags;
+    // nullptr: o goes to FwdArgs::o. Else to this [N, o_T, H, V] buffer, whose
+    // token 0 is token o_t0 of the row (the task writes tokens t - o_t0).
+    float* o;
+    int o_t0, o_T;
 };
 constexpr int kMaxTasks = 3;
 
@@ -46,6 +59,13 @@ struct FwdArgs {
 // from its transition map Pmap (K x K) and its zero-start end state R (K x V).
 hipError_t launch_affine_combine(const float* Pmap, const float* S_in, const float* R, float* S_out,
                                  int nchains, hipStream_t stream);
+
+// o[n, t, h, :] += S[n H + h]^T ell[n, t - t0, h, :] for t in [t0, T), every
+// row n < B and head h: the part of a slice's output due to its start state S,
+// from ell, the output of the same slice run from the identity with v = 0.
+// o is [B, T, H, V], ell [B, T - t0, H, K], S [B H, K, V], all fp32.
+hipError_t launch_state_correction(const float* S, const float* ell, float* o, int B, int T, int H, int t0,
+                                   hipStream_t stream);
 
 // One phase at a time (both input dtypes); used for fp32 inputs.
 int serial_workgroups(int nchains);

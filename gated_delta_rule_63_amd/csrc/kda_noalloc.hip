@@ -1,10 +1,13 @@
 // kda_noalloc.hip -- kda_fwd for callers that cannot allocate device memory.
 //
-// kda_fwd needs a workspace only on its three-slice route for few long chains
-// (four fp32 states per sequence and head). When the caller passes none, it
-// allocates one on the stream. kda_fwd_noalloc instead points that workspace at
-// `scratch`, a static device array of fixed size, and never calls an allocator.
+// kda_fwd needs a workspace only on its slice routes for few long chains. When
+// the caller passes none, it takes the three-slice route and allocates that
+// route's four fp32 states per sequence and head on the stream.
+// kda_fwd_noalloc instead points the workspace at `scratch`, a static device
+// array of fixed size, and never calls an allocator: kda_fwd then takes the
+// two-slice route when its workspace fits there, else the three-slice route.
 #include "../../include/kda.h"
+#include "kda_launch.h"
 
 #include <hip/hip_runtime.h>
 
@@ -52,7 +55,7 @@ kda_status_t kda_fwd_noalloc(const void* q, const void* k, const void* v, const 
     if (!desc) return KDA_ERR_NULL;
     // 0 for an invalid descriptor too: kda_fwd then reports the argument error.
     // Variable-length batches never take the slice route.
-    const size_t need = cu_seqlens ? 0 : kda_fwd_workspace_size(desc);
+    const size_t need = cu_seqlens ? 0 : kda::fwd_workspace_bytes(desc, true);
     if (need > kScratchBytes) return KDA_ERR_WORKSPACE;
     kda_desc_t d = *desc;
     d.workspace = nullptr;

@@ -19,6 +19,10 @@ hipError_t launch_affine_combine(const float*, const float*, const float*, float
     rec("affine_combine", nullptr);
     return hipSuccess;
 }
+hipError_t launch_state_correction(const float*, const float*, float*, int, int, int, int, hipStream_t) {
+    rec("state_correction", nullptr);
+    return hipSuccess;
+}
 int serial_workgroups(int nchains) { return nchains * 2; }
 hipError_t launch_fwd_serial(const FwdArgs& a, bool, hipStream_t) { rec("serial", &a); return hipSuccess; }
 int pipe_state_waves(int nchains, int cus) { return nchains * 8 <= cus ? 1 : nchains * 4 <= cus ? 2 : 4; }

@@ -129,16 +129,19 @@ def test_staged_layout(K):
 
 def test_fwd_workspace_size(K):
     """kda_fwd_workspace_size reports what kda_fwd itself uses: nothing for the
-    single fused launch, four 64 KiB fp32 states per (sequence, head) when few
-    long chains take the three-slice route (this machine has no GPU, so the
-    library assumes the MI355X's 256 compute units)."""
+    single fused launch; for few long chains the two-slice route's three 64 KiB
+    fp32 states per (sequence, head) and its fp32 ell for the second half
+    [B, T - T/2, H, 128] (this machine has no GPU, so the library assumes the
+    MI355X's 256 compute units)."""
     size = lambda d: K.lib().kda_fwd_workspace_size(ctypes.byref(d))
+    two = lambda B, T, H: B * H * 3 * 128 * 128 * 4 + B * (T - (T // 2) // 32 * 32) * H * 128 * 4
     assert size(desc(K, T=8192, H=96)) == 0                          # headline shape: one fused launch
     assert size(desc(K, T=8192, H=64)) == 0
     assert size(desc(K, T=8192, N=6, H=96)) == 0                     # varlen: never sliced
-    assert size(desc(K, T=131072, H=32)) == 32 * 4 * 128 * 128 * 4   # 8 MiB
-    assert size(desc(K, T=131072, H=32)) == 8 << 20
-    assert size(desc(K, T=65536, H=32)) == 8 << 20                   # each half of the 2 x 65536 handoff
+    assert size(desc(K, T=131072, H=32)) == two(1, 131072, 32)        # 6 MiB + 1 GiB
+    assert size(desc(K, T=131072, H=32)) == (6 << 20) + (1 << 30)
+    assert size(desc(K, T=65536, H=32)) == two(1, 65536, 32)          # each half of the 2 x 65536 handoff
+    assert size(desc(K, T=12301, B=2, H=3)) == two(2, 12301, 3)       # second slice from token 6144
     assert size(desc(K, T=12287, H=32)) == 0                         # too short to slice
     assert size(desc(K, T=131072, H=48)) == 0                        # more than one chain per six CUs
     assert size(desc(K, T=131072, H=32, in_dt=1)) == 0               # fp32 inputs run whole

@@ -3,9 +3,10 @@ against the fp64 oracle on every head: as one call, and as two calls of 65536
 tokens with the first call's final state handed over as the second's initial
 state. Both the pages' gate draw and a mild gate (g x 0.01, memory of about
 120 tokens) are run: with the pages' draw the state forgets within about 20
-tokens, so only the mild gate makes h0, the handover and the three-slice
-route's affine combine (slices start at tokens 43680 and 87360, or 21824 and
-43680 within each half) matter at full length."""
+tokens, so only the mild gate makes h0, the handover and the slice routes'
+affine combines (three slices: starting at tokens 43680 and 87360, or 21824
+and 43680 within each half; two slices: the second from token 65536, its
+outputs corrected by S1^T ell) matter at full length."""
 import numpy as np
 import pytest
 
@@ -40,10 +41,15 @@ def case(gate):
     return _cache[gate]
 
 
-def fwd(t):
+def fwd(t, route="three"):
+    """route "three": no workspace (the three-slice route); "two": a workspace of
+    fwd_workspace_size bytes (the two-slice route and its output correction)."""
     import torch
     import gated_delta_rule_63_amd as kda
-    o, hT = kda.fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], initial_state=t["h0"])
+    ws = None
+    if route == "two":
+        ws = torch.empty(kda.fwd_workspace_size(t["q"]), dtype=torch.uint8, device=t["q"].device)
+    o, hT = kda.fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], initial_state=t["h0"], workspace=ws)
     torch.cuda.synchronize()
     return o, hT
 
@@ -54,14 +60,16 @@ def halves(t):
     return first, second
 
 
+@pytest.mark.parametrize("route", ["two", "three"])
 @pytest.mark.parametrize("gate", ["bj", "mild"])
-def test_long_context_all_heads(gate):
+def test_long_context_all_heads(gate, route):
     inp, ro, rs = case(gate)
     t = to_device(inp, "bf16")
-    o, hT = fwd(t)
+    o, hT = fwd(t, route)
     eo, es = rel_err(o.cpu().numpy(), ro), rel_err(hT.cpu().numpy(), rs)
     tol_o, tol_s = TOL["bf16"]
-    log(f"[long] T=131072 H=32 gate={gate} all heads: err_o {eo:.3e} (tol {tol_o:.0e}) err_hT {es:.3e} (tol {tol_s:.0e})")
+    log(f"[long] T=131072 H=32 gate={gate} {route} slices, all heads: err_o {eo:.3e} (tol {tol_o:.0e}) "
+        f"err_hT {es:.3e} (tol {tol_s:.0e})")
     assert np.isfinite(eo) and np.isfinite(es)
     assert eo <= tol_o and es <= tol_s
 
