@@ -15,8 +15,9 @@
 
 namespace {
 
-// 8 MiB: the slice workspace of 32 (sequence, head) chains, e.g. one sequence
-// of 32 heads (the long-context workload T = 131072, H = 32).
+// 8 MiB: the three-slice workspace of 32 (sequence, head) chains, e.g. one
+// sequence of 32 heads (the long-context workload T = 131072, H = 32), or the
+// two-slice workspace of short enough ones (T = 12288, H = 1: 3.2 MiB).
 constexpr size_t kScratchBytes = size_t(8) << 20;
 
 // Each GPU the library runs on holds its own copy until the process ends.

@@ -123,23 +123,32 @@ kda_status_t kda_fwd_check(const void* q, const void* k, const void* v, const fl
  * 16-byte aligned o, h0, hT, it runs the decode kernel of kda_decode_step
  * instead.
  * Few long chains (bf16, no cu_seqlens, T >= 12288, at most one chain per six
- * compute units) are cut into three slices of whole 32-token chunks: the
- * middle slice's state map is affine, S_end = Pmap S_start + R, so it is run
- * from zero and from the identity alongside the first slice, and the later
- * slices then run from their true start states (two passes of a third of the
- * length each, plus one small product). That path needs 256 KiB per
- * (sequence, head) of device memory: desc->workspace when it is at least
- * kda_fwd_workspace_size(desc) bytes, else a stream-ordered allocation on
- * `stream`, freed on the same stream (if that allocation fails, the chains run
- * whole). Every other case needs no workspace. */
+ * compute units) are cut into slices of whole 32-token chunks. A slice's end
+ * state and its outputs are affine in the state it starts from (S_end =
+ * Pmap S_start + R; o = o from zero + S_start^T ell, with ell the slice's
+ * output from the identity with v = 0), so later slices are run from zero and
+ * from the identity alongside the first. Two routes:
+ *  - two slices: with desc->workspace of at least kda_fwd_workspace_size(desc)
+ *    bytes (three fp32 states per (sequence, head) and ell, fp32
+ *    [B, T - T2, H, 128], where T2 = T/2 rounded down to a multiple of 32): one
+ *    pass over half the length, then hT = Pmap S1 + R and the second half's o
+ *    corrected by S1^T ell;
+ *  - three slices: with a smaller workspace of at least 256 KiB per
+ *    (sequence, head), or none (then a stream-ordered allocation of that size
+ *    on `stream`, freed on the same stream; if that allocation fails, the
+ *    chains run whole): two passes of a third of the length each.
+ * Every other case needs no workspace. */
 kda_status_t kda_fwd(const void* q, const void* k, const void* v, const float* g,
                      const float* beta, const int32_t* cu_seqlens, const float* h0,
                      void* o, float* hT, const kda_desc_t* desc, void* stream);
 
-/* Bytes of device workspace kda_fwd (and kda_gdn_fwd) uses for this
- * descriptor on the current device: 262,144 per (sequence, head) when the
- * three-slice route for few long chains applies (bf16, T >= 12288, at most one
- * chain per six compute units of the current device, no cu_seqlens), else 0.
+/* Bytes of device workspace kda_fwd (and kda_gdn_fwd) takes for this
+ * descriptor on the current device with its two-slice route for few long
+ * chains (bf16, T >= 12288, at most one chain per six compute units of the
+ * current device, no cu_seqlens): 196,608 per (sequence, head) plus
+ * 512 * B * (T - T2) * H with T2 = T/2 rounded down to a multiple of 32;
+ * else 0. A workspace of 262,144 per (sequence, head) up to this size runs the
+ * three-slice route without allocating.
  * The descriptor does not say whether cu_seqlens will be passed; with B ==
  * num_seqs == 1 the fixed-length answer is returned, which is never smaller
  * than what a varlen call needs. 0 also for an invalid descriptor. Host only;
@@ -150,12 +159,13 @@ size_t kda_fwd_workspace_size(const kda_desc_t* desc);
  * kda_fwd for callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation. Arguments,
  * layouts, results and errors as kda_fwd; desc->workspace is ignored. The
- * workspace kda_fwd would allocate (kda_fwd_workspace_size(desc) bytes, only
- * for the three-slice route) comes from a static device array of
- * kda_fwd_noalloc_max_workspace() bytes (8 MiB: 32 sequence-heads on that
- * route) that each GPU holds from the first call on it until the process ends.
- * A descriptor that needs more returns KDA_ERR_WORKSPACE before anything is
- * enqueued. No hipMalloc, hipFree or other allocating call is made.
+ * slice routes' workspace comes from a static device array of
+ * kda_fwd_noalloc_max_workspace() bytes (8 MiB) that each GPU holds from the
+ * first call on it until the process ends: the two-slice route when
+ * kda_fwd_workspace_size(desc) fits there, else the three-slice route (256 KiB
+ * per sequence-head: up to 32). A descriptor whose three-slice workspace does
+ * not fit either returns KDA_ERR_WORKSPACE before anything is enqueued. No
+ * hipMalloc, hipFree or other allocating call is made.
  * Every call on one GPU shares that GPU's array: calls that overlap on one GPU
  * (on different streams or host threads, or with the array still in use by an
  * earlier call's kernels on another stream) race and give undefined results.
