@@ -153,7 +153,9 @@ hipError_t run_two_slices(const kda::FwdArgs& a, const kda_desc_t* d, int cus, h
 }
 
 hipError_t run_slices(const kda::FwdArgs& a, const kda_desc_t* d, int cus, hipStream_t s) {
-    if (d->workspace && d->workspace_bytes >= slice2_workspace_bytes(d)) return run_two_slices(a, d, cus, s);
+    // the output correction reads ell in 16-byte pieces
+    if (d->workspace && d->workspace_bytes >= slice2_workspace_bytes(d) && aligned16(d->workspace))
+        return run_two_slices(a, d, cus, s);
     const size_t per = (size_t)a.nchains * 128 * 128;
     const size_t bytes = slice_workspace_bytes(a.nchains);
     void* ws = nullptr;
