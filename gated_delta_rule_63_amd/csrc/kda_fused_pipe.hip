@@ -293,11 +293,13 @@ __device__ __forceinline__ void factors(Smem& sm, Ops& op, Fac& fc, HFetch& f, H
     const int c0 = hchan(hw, cp);
 
     float L[2][SEG], kv[2][SEG], qv[2][SEG];
-    float r0 = 0.f, r1 = 0.f;
+    float r0 = f.g[0].x, r1 = f.g[0].y;
 #pragma unroll
     for (int t = 0; t < SEG; ++t) {
-        r0 += f.g[t].x;
-        r1 += f.g[t].y;
+        if (t > 0) {
+            r0 += f.g[t].x;
+            r1 += f.g[t].y;
+        }
         L[0][t] = r0;
         L[1][t] = r1;
         const float2 k2 = bf2(f.k[t]), q2 = bf2(f.q[t]);
@@ -633,11 +635,11 @@ __device__ __forceinline__ void state_products(const f32x4 (&S)[8], const Ops& o
 // State waves, second step of a chunk (after the mid-chunk barrier): the
 // solve Delta = (I + A)^{-1} Diag(beta) (V - P) over the two diagonal blocks,
 // the output O = O1 + M Delta stored through `ro`, and the state update
-// S <- Diag(gamma_last) S + Kt^T Delta. bt0, bt1 (beta) and ah (A10) were read
+// S <- Diag(gamma_last) S + Kt^T Delta. bt0, bt1 (beta) and a10 (A10) were read
 // before the barrier; vcur holds V of the wave's column (raw bf16 bits).
 __device__ __forceinline__ void state_finish(f32x4 (&S)[8], const Ops& op, const f32x4 (&Pt)[2], const f32x4 (&Ot)[2],
                                              const uint32_t (&vcur)[8], const float4& bt0, const float4& bt1,
-                                             const f16x8& ah, __amdgpu_buffer_rsrc_t ro, const uint32_t (&voff)[8],
+                                             const f16x4& a10, __amdgpu_buffer_rsrc_t ro, const uint32_t (&voff)[8],
                                              int l16, int grp) {
     const float bts[2][4] = {{bt0.x, bt0.y, bt0.z, bt0.w}, {bt1.x, bt1.y, bt1.z, bt1.w}};
     float be[2][4];
@@ -646,34 +648,29 @@ __device__ __forceinline__ void state_finish(f32x4 (&S)[8], const Ops& op, const
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             be[t][j] = bts[t][j] * (__uint_as_float(vcur[4 * t + j] << 16) - Pt[t][j]);
-    // Delta0 = T00 bE0 (two-term fp16 operand; slots of sub-block 1 are zero)
-    uint32_t bh[4] = {0u, 0u, 0u, 0u}, bl[4] = {0u, 0u, 0u, 0u};
+    // The solve runs on 16x16x16 MFMAs: the A operand is the half of a row's
+    // 16-byte kperm piece that holds the block's columns 4grp..4grp+3, the B
+    // operand four halves (tokens 4grp+j of one sub-block, column l16).
+    // Delta0 = T00 bE0 (two-term fp16 operand)
+    const f32x4 Z = {0.f, 0.f, 0.f, 0.f};
+    uint32_t bh[2], bl[2];
     split_f16x2(be[0][0], be[0][1], bh[0], bl[0]);
     split_f16x2(be[0][2], be[0][3], bh[1], bl[1]);
-    f32x4 D0 = {0.f, 0.f, 0.f, 0.f};
-    {
-        const f16x8 th = lds_vec<f16x8>(&op.Tm[l16][tcol(l16, 8 * grp)]);
-        D0 = mfma16(th, __builtin_bit_cast(f16x8, bh), D0);
-        D0 = mfma16(th, __builtin_bit_cast(f16x8, bl), D0);
-    }
-    uint32_t dh[4] = {0u, 0u, 0u, 0u}, dl[4] = {0u, 0u, 0u, 0u};
+    const f16x4 t00 = lds_vec<f16x4>(&op.Tm[l16][tcol(l16, 8 * grp)]);
+    f32x4 D0 = __builtin_amdgcn_mfma_f32_16x16x16f16(t00, __builtin_bit_cast(f16x4, bh), Z, 0, 0, 0);
+    D0 = __builtin_amdgcn_mfma_f32_16x16x16f16(t00, __builtin_bit_cast(f16x4, bl), D0, 0, 0, 0);
+    uint32_t dh[4], dl[4];
     split_f16x2(D0[0], D0[1], dh[0], dl[0]);
     split_f16x2(D0[2], D0[3], dh[1], dl[1]);
     // Delta1 = T11 (bE1 - A10 Delta0)
-    f32x4 X = {0.f, 0.f, 0.f, 0.f};
-    {
-        X = mfma16(ah, __builtin_bit_cast(f16x8, dh), X);
-        X = mfma16(ah, __builtin_bit_cast(f16x8, dl), X);
-    }
-    bh[0] = bh[1] = bl[0] = bl[1] = 0u;
-    split_f16x2(be[1][0] - X[0], be[1][1] - X[1], bh[2], bl[2]);
-    split_f16x2(be[1][2] - X[2], be[1][3] - X[3], bh[3], bl[3]);
-    f32x4 D1 = {0.f, 0.f, 0.f, 0.f};
-    {
-        const f16x8 th = lds_vec<f16x8>(&op.Tm[16 + l16][tcol(l16, 8 * grp)]);
-        D1 = mfma16(th, __builtin_bit_cast(f16x8, bh), D1);
-        D1 = mfma16(th, __builtin_bit_cast(f16x8, bl), D1);
-    }
+    const uint2 d0h = make_uint2(dh[0], dh[1]), d0l = make_uint2(dl[0], dl[1]);
+    f32x4 X = __builtin_amdgcn_mfma_f32_16x16x16f16(a10, __builtin_bit_cast(f16x4, d0h), Z, 0, 0, 0);
+    X = __builtin_amdgcn_mfma_f32_16x16x16f16(a10, __builtin_bit_cast(f16x4, d0l), X, 0, 0, 0);
+    split_f16x2(be[1][0] - X[0], be[1][1] - X[1], bh[0], bl[0]);
+    split_f16x2(be[1][2] - X[2], be[1][3] - X[3], bh[1], bl[1]);
+    const f16x4 t11 = lds_vec<f16x4>(&op.Tm[16 + l16][tcol(l16, 8 * grp) + 4]);
+    f32x4 D1 = __builtin_amdgcn_mfma_f32_16x16x16f16(t11, __builtin_bit_cast(f16x4, bh), Z, 0, 0, 0);
+    D1 = __builtin_amdgcn_mfma_f32_16x16x16f16(t11, __builtin_bit_cast(f16x4, bl), D1, 0, 0, 0);
     split_f16x2(D1[0], D1[1], dh[2], dl[2]);
     split_f16x2(D1[2], D1[3], dh[3], dl[3]);
     const f16x8 DBh = __builtin_bit_cast(f16x8, dh), DBl = __builtin_bit_cast(f16x8, dl);
@@ -861,7 +858,7 @@ __global__ __launch_bounds__(64 * (NS + NH), 1) void kda_fwd_pipe(FwdArgs a) {
             // read them now, so the solve after the barrier starts without an
             // LDS round trip (T is written in this phase and is read after it).
             const float4 bt0 = lds_vec<float4>(&op.beta[4 * grp]), bt1 = lds_vec<float4>(&op.beta[16 + 4 * grp]);
-            const f16x8 ah = lds_vec<f16x8>(&op.A10[l16][tcol(l16, 8 * grp)]);
+            const f16x4 ah = lds_vec<f16x4>(&op.A10[l16][tcol(l16, 8 * grp)]);   // A10 row l16, columns 4grp..4grp+3
             __syncthreads();   // mid-chunk: the helpers' factors of chunk ci+1 are written
             // O's rows past the chunk's end are dropped; an empty resource drops
             // every store (a slice run for its state only)
@@ -1096,7 +1093,7 @@ void kda_recur_pipe(FwdArgs a, const uint4* rec, int nch) {
             f32x4 Pt[2], Ot[2];
             state_products(S, op, ops[ci & 1].rec, l16, grp, Pt, Ot);
             const float4 bt0 = lds_vec<float4>(&op.beta[4 * grp]), bt1 = lds_vec<float4>(&op.beta[16 + 4 * grp]);
-            const f16x8 ah = lds_vec<f16x8>(&op.A10[l16][tcol(l16, 8 * grp)]);
+            const f16x4 ah = lds_vec<f16x4>(&op.A10[l16][tcol(l16, 8 * grp)]);   // A10 row l16, columns 4grp..4grp+3
             const auto ro = chunk_rsrc(a.o, base + (long long)cs * ts, 4, nv, ts, D);
             state_finish(S, op, Pt, Ot, vcur, bt0, bt1, ah, ro, voff, l16, grp);
             vunpack(vcur, vraw, vc & 1);
