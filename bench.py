@@ -103,6 +103,32 @@ def calib_copy(args):
     print(f"[bench] calibration copy of {nbytes} bytes done", file=sys.stderr, flush=True)
 
 
+def copy_bandwidth(nbytes: int = 1 << 30, reps: int = 20):
+    """Device-to-device copy bandwidth on this GPU (bytes read plus bytes written
+    per second, GB/s), timed with events over `reps` copies of `nbytes` after
+    three untimed ones: the practical HBM ceiling the roofline fraction is also
+    quoted against."""
+    import torch
+    try:
+        src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+    except RuntimeError:
+        return None
+    src.fill_(1)
+    for _ in range(3):
+        dst.copy_(src)
+    stream = torch.cuda.current_stream()
+    a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a_.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    b_.record(stream)
+    torch.cuda.synchronize()
+    sec = a_.elapsed_time(b_) / 1e3 / reps
+    del src, dst
+    return 2 * nbytes / sec / 1e9
+
+
 def bench_decode(args):
     """In-place decode steps: N sequences x 96 heads, one token each per step."""
     import numpy as np
@@ -346,6 +372,7 @@ def main():
         log(f"[bench] stages: {stage_times}")
 
     calib_copy(args)
+    copy_gbs = copy_bandwidth()
 
     tokens = cfg.B * cfg.T
     value = tokens / (ms / 1e3)
@@ -376,6 +403,7 @@ def main():
         cpu = {"value": tokens * runs / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
                "sample": f"the whole {cfg.name} workload ({cfg.token_heads} token-heads) {runs} times, {dt:.1f} s",
                "host": host_description()}
+        cpu["gpu_over_oracle"] = value / cpu["value"]
 
     desc = f"{cfg.name}: B={cfg.B} T={cfg.T} H={cfg.H} K=V=128 {cfg.dtype} q/k/v, fp32 g/beta/state"
     if cfg.seq_lens:
@@ -390,7 +418,8 @@ def main():
                    "global_batch": cfg.B, "seq_len": cfg.T, "heads": cfg.H, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": kname, "alg_bytes_per_launch": bytes_},
+                     "kernel": kname, "alg_bytes_per_launch": bytes_,
+                     "copy_GBs": copy_gbs, "frac_of_copy": achieved / copy_gbs if copy_gbs else None},
         "mfma": {"achieved": flops / (ms / 1e3) / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": flops / (ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
         "protocol": {"repeats": len(reps), "iters": args.steps, "median_ms": float(np.median(reps)) if reps else None,

@@ -93,10 +93,12 @@ def test_worked_example_embedded():
 
 
 # ---------------------------------------------------------------- full-size workloads
+# every head, three seeds each (seed 0 is also the timed draw)
+@pytest.mark.parametrize("seed", [0, 1, 2])
 @pytest.mark.parametrize("name", ["T8192_H64", "T8192_H96", "varlen6_T8192_H96", "varlen8x1024_H96"])
-def test_full_config(name):
-    log(f"[full] {name}: generating inputs")
-    check(W.make_inputs(W.CONFIGS[name], 0), what=f"{name} full")
+def test_full_config(name, seed):
+    log(f"[full] {name} seed {seed}: generating inputs")
+    check(W.make_inputs(W.CONFIGS[name], seed), what=f"{name} full seed {seed}")
 
 
 # T = 131072, H = 32 (all heads, and as 2 x 65536 with the state handed over) is in test_gpu_long.py.
