@@ -45,10 +45,12 @@ namespace pipe {
 
 constexpr int C = 32;          // chunk length (two 16-token sub-blocks)
 constexpr int NH = 8;          // helper waves, 16 channels each
-// NS state waves (16 V columns each) per workgroup: 4, 2 or 1, so a (sequence,
-// head) is split over P = 2, 4 or 8 workgroups. Every split computes the same
-// values in the same order per column; a finer split only repeats the helper
-// work, which pays when there are too few chains to fill the chip.
+// NS state waves (16 V columns each) per workgroup: 8, 4, 2 or 1, so a
+// (sequence, head) is split over P = 1, 2, 4 or 8 workgroups. Every split
+// computes the same values in the same order per column; a finer split only
+// repeats the helper work, which pays when there are too few chains to fill
+// the chip. With more chains than the chip holds at P = 2, P = 1 (sixteen
+// waves, four per SIMD) does each chain's helper work once.
 template <int NS>
 struct Split {
     static constexpr int NT = 64 * (NS + NH);   // threads per workgroup
@@ -569,6 +571,7 @@ __device__ __forceinline__ void tile_block(const Fac& fc, Ops& op, const HStage&
 // phase short.
 //   NS = 4: every SIMD holds a state wave, and SIMDs 0 and 1 also run the
 //           inverses: one block each there, two each on the other two;
+//   NS = 8: the same with two state waves per SIMD;
 //   NS = 2: two blocks on each of the two SIMDs without a state wave, one on
 //           each of the others;
 //   NS = 1: one block on each helper wave of the three SIMDs without the state wave.
@@ -577,7 +580,7 @@ __device__ __forceinline__ void tile_block(const Fac& fc, Ops& op, const HStage&
 // for the input prefetch.
 template <int NS>
 __device__ __forceinline__ int helper_block(int hw) {
-    constexpr uint64_t T = NS == 4 ? 0x0504FFFF03020100ull : (NS == 2 ? 0xFFFF050304020100ull : 0xFF050301FF040200ull);
+    constexpr uint64_t T = (NS == 4 || NS == 8) ? 0x0504FFFF03020100ull : (NS == 2 ? 0xFFFF050304020100ull : 0xFF050301FF040200ull);
     return (int)((T >> (8 * hw)) & 0xFFu);
 }
 
@@ -1156,7 +1159,7 @@ hipError_t launch_fwd_two_pass(const FwdArgs& a, void* workspace, int cus, hipSt
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const int ns = pipe_state_waves(a.nchains, cus);
+    const int ns = min(4, pipe_state_waves(a.nchains, cus));   // the ablation keeps P >= 2
     const dim3 g3(pipe_workgroups(a.nchains, ns));
     if (ns == 1) hipLaunchKernelGGL((pipe::kda_recur_pipe<1>), g3, dim3(64 * (1 + pipe::NCW)), 0, stream, a, rec, nch);
     else if (ns == 2) hipLaunchKernelGGL((pipe::kda_recur_pipe<2>), g3, dim3(64 * (2 + pipe::NCW)), 0, stream, a, rec, nch);
@@ -1167,7 +1170,8 @@ hipError_t launch_fwd_two_pass(const FwdArgs& a, void* workspace, int cus, hipSt
 int pipe_state_waves(int nchains, int cus) {
     if ((long long)nchains * 8 <= cus) return 1;
     if ((long long)nchains * 4 <= cus) return 2;
-    return 4;
+    if ((long long)nchains * 2 <= cus) return 4;
+    return 8;
 }
 
 int pipe_workgroups(int nchains, int state_waves) {
@@ -1183,11 +1187,13 @@ hipError_t launch_fwd_pipe(const FwdArgs& a, int cus, hipStream_t stream) {
     if (a.scalar_gate) {
         if (ns == 1) hipLaunchKernelGGL((pipe::kda_fwd_pipe<1, true>), g3, dim3(pipe::Split<1>::NT), 0, stream, a);
         else if (ns == 2) hipLaunchKernelGGL((pipe::kda_fwd_pipe<2, true>), g3, dim3(pipe::Split<2>::NT), 0, stream, a);
-        else hipLaunchKernelGGL((pipe::kda_fwd_pipe<4, true>), g3, dim3(pipe::Split<4>::NT), 0, stream, a);
+        else if (ns == 4) hipLaunchKernelGGL((pipe::kda_fwd_pipe<4, true>), g3, dim3(pipe::Split<4>::NT), 0, stream, a);
+        else hipLaunchKernelGGL((pipe::kda_fwd_pipe<8, true>), g3, dim3(pipe::Split<8>::NT), 0, stream, a);
     } else {
         if (ns == 1) hipLaunchKernelGGL((pipe::kda_fwd_pipe<1, false>), g3, dim3(pipe::Split<1>::NT), 0, stream, a);
         else if (ns == 2) hipLaunchKernelGGL((pipe::kda_fwd_pipe<2, false>), g3, dim3(pipe::Split<2>::NT), 0, stream, a);
-        else hipLaunchKernelGGL((pipe::kda_fwd_pipe<4, false>), g3, dim3(pipe::Split<4>::NT), 0, stream, a);
+        else if (ns == 4) hipLaunchKernelGGL((pipe::kda_fwd_pipe<4, false>), g3, dim3(pipe::Split<4>::NT), 0, stream, a);
+        else hipLaunchKernelGGL((pipe::kda_fwd_pipe<8, false>), g3, dim3(pipe::Split<8>::NT), 0, stream, a);
     }
     return hipGetLastError();
 }

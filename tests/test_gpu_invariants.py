@@ -116,18 +116,19 @@ def test_linear_in_q():
 
 
 def test_split_over_workgroups_is_bitwise():
-    """The number of workgroups a head is split over (2, 4 or 8, chosen from the
-    number of chains) does not change any value: heads 0-19 of an 80-head run
-    (two-way split) equal the same heads run as a 20-head (eight-way) and a
-    40-head (four-way) problem."""
+    """The number of workgroups a head is split over (1, 2, 4 or 8, chosen from
+    the number of chains on a 256-CU chip) does not change any value: a 160-head
+    run (one workgroup per head, sixteen waves) equals the same heads run as an
+    80-head (two-way split), a 40-head (four-way) and a 20-head (eight-way)
+    problem."""
     import torch
-    cfg = W.variant("T8192_H96", T=300, H=80, h0=True, gate="mild", name="split-ways")
+    cfg = W.variant("T8192_H96", T=300, H=160, h0=True, gate="mild", name="split-ways")
     t = to_device(W.make_inputs(cfg, 8), "bf16")
-    o80, h80 = fwd(t)
-    for H in (20, 40):
+    o160, h160 = fwd(t)
+    for H in (20, 40, 80):
         sub = {k: (v[:, :, :H].contiguous() if k in ("q", "k", "v", "g", "beta") else v) for k, v in t.items()}
         sub["h0"] = t["h0"][:, :H].contiguous()
         o, h = fwd(sub)
-        log(f"[split] H={H}: max|o - o80| = {float((o - o80[:, :, :H]).abs().max()):.3g}")
-        assert bool((o == o80[:, :, :H]).all()), f"H={H} output"
-        assert bool((h == h80[:, :H]).all()), f"H={H} state"
+        log(f"[split] H={H}: max|o - o160| = {float((o - o160[:, :, :H]).abs().max()):.3g}")
+        assert bool((o == o160[:, :, :H]).all()), f"H={H} output"
+        assert bool((h == h160[:, :H]).all()), f"H={H} state"
