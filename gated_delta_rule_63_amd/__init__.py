@@ -120,7 +120,7 @@ def noalloc_max_workspace() -> int:
 def fwd_workspace_size(q: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None) -> int:
     """Bytes of device workspace fwd() / gdn_fwd() use for inputs shaped like q
     (kda_fwd_workspace_size; 0 for most shapes). For few long chains, a workspace
-    of at least this size selects the faster two-slice route and keeps fwd()
+    of at least this size selects the faster one-pass slice route and keeps fwd()
     from allocating; without one, fwd() allocates the three-slice route's."""
     return int(lib().kda_fwd_workspace_size(ctypes.byref(_desc(q, cu_seqlens))))
 

@@ -106,11 +106,14 @@ constexpr int kMinSlice = 4096;   // tokens per slice before a chain is cut into
 // state map and its outputs are affine in the state it starts from, so a
 // chain is cut into slices of whole chunks, each later slice run from zero and
 // from the identity alongside the first. Two routes:
-//   two slices (desc->workspace of slice2_workspace_bytes): one pass runs
-//     slice 0 for real and slice 1 from zero (o into o) and from the identity
-//     with v = 0 (its o, ell, into the workspace; its end state is Pmap1);
-//     then hT = Pmap1 S1 + R1, and o of slice 1 += S1^T ell per token. The
-//     critical path is half a chain plus a streaming pass over slice 1's o.
+//   S slices in one pass (desc->workspace of multi_slice_workspace_bytes):
+//     one launch runs slice 0 for real and every later slice j from zero (o
+//     into o, end state R_j) and from the identity with v = 0 (its o, ell,
+//     into the workspace; its end state is Pmap_j), one workgroup per run, so
+//     that all 2S - 1 runs of every chain fit on the chip together (S = 4 for
+//     32 chains on 256 CUs). Then S_{j+1} = Pmap_j S_j + R_j in turn (the last
+//     one is hT), and o of slice j += S_j^T ell per token. The critical path
+//     is 1/S of a chain plus a streaming pass over the later slices' o.
 //   three slices (less workspace, or none: 256 KiB per chain, allocated on
 //     the stream when not given): pass 1 runs slice 0 for real and slice 1
 //     from zero and from the identity; a combine forms slice 2's start state;
@@ -123,39 +126,62 @@ bool use_slices(long long nchains, const kda_desc_t* d, bool varlen, int cus) {
 // Workspace of the three-slice route: four fp32 states per chain (S1, R1, Pmap1, S2).
 size_t slice_workspace_bytes(long long nchains) { return (size_t)nchains * 4 * 128 * 128 * sizeof(float); }
 
-// First token of the two-slice route's second slice.
-int slice2_split(int T) { return (T / 2) / 32 * 32; }
-
-// Workspace of the two-slice route: three fp32 states per chain (S1, R1,
-// Pmap1) and ell, fp32 [B, T - split, H, 128].
-size_t slice2_workspace_bytes(const kda_desc_t* d) {
-    const size_t states = (size_t)d->B * d->H * 3 * 128 * 128 * sizeof(float);
-    return states + (size_t)d->B * (d->T - slice2_split(d->T)) * d->H * 128 * sizeof(float);
+// Slice count of the one-pass route: each slice after the first runs twice,
+// one workgroup per run, and the 2S - 1 runs of all chains must fit on the
+// chip at once; each slice keeps at least kMinSlice tokens. At least 2.
+constexpr int kMaxSlices = (kda::kMaxTasks + 1) / 2;
+int multi_slice_count(long long nchains, int T, int cus) {
+    long long n = (cus / nchains + 1) / 2;
+    n = std::min<long long>(n, kMaxSlices);
+    n = std::min<long long>(n, T / kMinSlice);
+    return (int)std::max<long long>(n, 2);
 }
 
-hipError_t run_two_slices(const kda::FwdArgs& a, const kda_desc_t* d, int cus, hipStream_t s) {
+// First token of slice j of S (whole chunks; slice S starts at T).
+int slice_begin(int T, int S, int j) { return j >= S ? T : (int)(((long long)j * T / S) / 32 * 32); }
+
+// Workspace of the one-pass route: three fp32 states per chain and later
+// slice (its start state S_j, R_j and Pmap_j) and ell, fp32
+// [B, T - (first token of slice 1), H, 128].
+size_t multi_slice_workspace_bytes(const kda_desc_t* d, int S) {
+    const size_t states = (size_t)d->B * d->H * 3 * (S - 1) * 128 * 128 * sizeof(float);
+    return states + (size_t)d->B * (d->T - slice_begin(d->T, S, 1)) * d->H * 128 * sizeof(float);
+}
+
+hipError_t run_multi_slices(const kda::FwdArgs& a, const kda_desc_t* d, int S, int cus, hipStream_t s) {
     const size_t per = (size_t)a.nchains * 128 * 128;
-    float* S1 = static_cast<float*>(d->workspace);   // state after slice 0
-    float* R1 = S1 + per;                             // slice 1 from zero
-    float* P1 = R1 + per;                             // slice 1's transition map
-    float* ell = P1 + per;                            // slice 1's o from the identity
-    const int T = d->T, s1 = slice2_split(T);
+    float* const ws = static_cast<float*>(d->workspace);
+    const auto start = [&](int j) { return ws + (size_t)(j - 1) * per; };            // S_j, slice j's start state
+    const auto zero = [&](int j) { return ws + (size_t)(S - 1 + j - 1) * per; };      // R_j, slice j from zero
+    const auto pmap = [&](int j) { return ws + (size_t)(2 * (S - 1) + j - 1) * per; };  // Pmap_j
+    float* ell = ws + (size_t)3 * (S - 1) * per;                                     // o of the identity runs
+    const int T = d->T, b1 = slice_begin(T, S, 1);
     kda::FwdArgs p = a;
-    p.ntasks = 3;
-    p.nchains = 3 * a.nchains;
-    p.task[0] = {0, s1, a.h0, S1, 0};
-    p.task[1] = {s1, T, nullptr, R1, 0};
-    p.task[2] = {s1, T, nullptr, P1, kda::TASK_ZERO_V | kda::TASK_IDENTITY_H0, ell, s1, T - s1};
+    p.ntasks = 2 * S - 1;
+    p.nchains = p.ntasks * a.nchains;
+    p.task[0] = {0, b1, a.h0, start(1), 0};
+    for (int j = 1; j < S; ++j) {
+        const int t0 = slice_begin(T, S, j), t1 = slice_begin(T, S, j + 1);
+        p.task[2 * j - 1] = {t0, t1, nullptr, zero(j), 0};
+        p.task[2 * j] = {t0, t1, nullptr, pmap(j), kda::TASK_ZERO_V | kda::TASK_IDENTITY_H0, ell, b1, T - b1};
+    }
     hipError_t e = kda::launch_fwd_pipe(p, cus, s);
-    if (e == hipSuccess && a.hT) e = kda::launch_affine_combine(P1, S1, R1, a.hT, a.nchains, s);
-    if (e == hipSuccess) e = kda::launch_state_correction(S1, ell, a.o, a.N, T, a.H, s1, s);
+    // the later slices' start states in turn; the last combine is the final state
+    for (int j = 1; j < S && e == hipSuccess; ++j) {
+        float* out = j + 1 < S ? start(j + 1) : a.hT;
+        if (out) e = kda::launch_affine_combine(pmap(j), start(j), zero(j), out, a.nchains, s);
+    }
+    for (int j = 1; j < S && e == hipSuccess; ++j)
+        e = kda::launch_state_correction(start(j), ell, a.o, a.N, T, a.H, slice_begin(T, S, j),
+                                         slice_begin(T, S, j + 1), b1, s);
     return e;
 }
 
 hipError_t run_slices(const kda::FwdArgs& a, const kda_desc_t* d, int cus, hipStream_t s) {
     // the output correction reads ell in 16-byte pieces
-    if (d->workspace && d->workspace_bytes >= slice2_workspace_bytes(d) && aligned16(d->workspace))
-        return run_two_slices(a, d, cus, s);
+    const int S = multi_slice_count(a.nchains, d->T, cus);
+    if (d->workspace && d->workspace_bytes >= multi_slice_workspace_bytes(d, S) && aligned16(d->workspace))
+        return run_multi_slices(a, d, S, cus, s);
     const size_t per = (size_t)a.nchains * 128 * 128;
     const size_t bytes = slice_workspace_bytes(a.nchains);
     void* ws = nullptr;
@@ -316,8 +342,9 @@ size_t fwd_workspace_bytes(const kda_desc_t* desc, bool smallest) {
     if (desc->T == 1) return 0;   // the decode route
     const long long nchains = (long long)desc->num_seqs * desc->H;
     if (!maybe_fixed || !use_slices(nchains, desc, false, device_cus())) return 0;
-    const size_t two = slice2_workspace_bytes(desc), three = slice_workspace_bytes(nchains);
-    return smallest ? std::min(two, three) : two;
+    const int S = multi_slice_count(nchains, desc->T, device_cus());
+    const size_t one_pass = multi_slice_workspace_bytes(desc, S), three = slice_workspace_bytes(nchains);
+    return smallest ? std::min(one_pass, three) : one_pass;
 }
 
 }  // namespace kda

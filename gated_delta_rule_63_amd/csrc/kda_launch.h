@@ -9,7 +9,7 @@ struct kda_desc;
 
 namespace kda {
 
-// Device workspace kda_fwd uses for this descriptor: the two-slice route's
+// Device workspace kda_fwd uses for this descriptor: the one-pass slice route's
 // (what kda_fwd_workspace_size reports), or with `smallest` the least any
 // route takes without allocating (the three-slice route's when that is
 // smaller). 0 where no route needs any, and for an invalid descriptor.
@@ -33,7 +33,7 @@ struct FwdTask {
     float* o;
     int o_t0, o_T;
 };
-constexpr int kMaxTasks = 3;
+constexpr int kMaxTasks = 7;   // slice runs per chain in one launch: 1 + 2 * 3
 
 struct FwdArgs {
     const void* q;
@@ -60,19 +60,21 @@ struct FwdArgs {
 hipError_t launch_affine_combine(const float* Pmap, const float* S_in, const float* R, float* S_out,
                                  int nchains, hipStream_t stream);
 
-// o[n, t, h, :] += S[n H + h]^T ell[n, t - t0, h, :] for t in [t0, T), every
+// o[n, t, h, :] += S[n H + h]^T ell[n, t - e0, h, :] for t in [t0, t1), every
 // row n < B and head h: the part of a slice's output due to its start state S,
 // from ell, the output of the same slice run from the identity with v = 0.
-// o is [B, T, H, V], ell [B, T - t0, H, K], S [B H, K, V], all fp32.
+// o is [B, T, H, V], ell [B, T - e0, H, K] (tokens e0 .. T - 1, e0 <= t0), S
+// [B H, K, V], all fp32.
 hipError_t launch_state_correction(const float* S, const float* ell, float* o, int B, int T, int H, int t0,
-                                   hipStream_t stream);
+                                   int t1, int e0, hipStream_t stream);
 
 // One phase at a time (both input dtypes); used for fp32 inputs.
 int serial_workgroups(int nchains);
 hipError_t launch_fwd_serial(const FwdArgs& a, bool f32_inputs, hipStream_t stream);
 // Helper waves prepare chunk i+1 while state waves advance chunk i (bf16 inputs).
 // The chain is split over 128 / (16 * state_waves) workgroups; state_waves is
-// 4, 2 or 1, the largest that still fills `cus` compute units.
+// 4, 2 or 1, the largest that still fills `cus` compute units, or 8 (one
+// workgroup per chain) when two workgroups per chain would not fit on them.
 int pipe_state_waves(int nchains, int cus);
 int pipe_workgroups(int nchains, int state_waves);
 hipError_t launch_fwd_pipe(const FwdArgs& a, int cus, hipStream_t stream);

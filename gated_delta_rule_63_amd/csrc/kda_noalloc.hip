@@ -5,7 +5,7 @@
 // route's four fp32 states per sequence and head on the stream.
 // kda_fwd_noalloc instead points the workspace at `scratch`, a static device
 // array of fixed size, and never calls an allocator: kda_fwd then takes the
-// two-slice route when its workspace fits there, else the three-slice route.
+// one-pass slice route when its workspace fits there, else the three-slice route.
 #include "../../include/kda.h"
 #include "kda_launch.h"
 
@@ -17,7 +17,8 @@ namespace {
 
 // 8 MiB: the three-slice workspace of 32 (sequence, head) chains, e.g. one
 // sequence of 32 heads (the long-context workload T = 131072, H = 32), or the
-// two-slice workspace of short enough ones (T = 12288, H = 1: 3.2 MiB).
+// one-pass workspace of short enough ones (T = 12288, H = 1, three slices:
+// 4.4 MiB).
 constexpr size_t kScratchBytes = size_t(8) << 20;
 
 // Each GPU the library runs on holds its own copy until the process ends.

@@ -58,18 +58,18 @@ __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uin
 
 constexpr int TB = 256;   // tokens per workgroup: four steps of the four waves' 16 tokens
 
-// o[n, t0 + t, h, :] += S^T ell[n, t, h, :] for one (row n, head h) and TB
-// tokens t. ell (A operand: 16 tokens x 32 channels per MFMA) and S (B
+// o[n, t, h, :] += S^T ell[n, t - e0, h, :] for one (row n, head h) and TB
+// tokens t of [t0, t1); ell holds tokens e0 .. T - 1 of each row. ell (A operand: 16 tokens x 32 channels per MFMA) and S (B
 // operand: 32 channels x 16 columns) each enter as two bf16 terms, three MFMA
 // terms with fp32 accumulation onto o. S is staged once per workgroup in LDS
 // as the B operands of its eight 16-column tiles and four 32-channel steps,
 // one 16-byte piece per lane, so each lane reads its own piece.
 __global__ __launch_bounds__(256) void state_correction_kernel(const float* __restrict__ S,
                                                               const float* __restrict__ ell, float* __restrict__ o,
-                                                              int T, int H, int t0) {
+                                                              int T, int H, int t0, int t1, int e0) {
     __shared__ uint4 Bh[8][4][64], Bl[8][4][64];
     const int chain = blockIdx.y, n = chain / H, h = chain % H;
-    const int Tc = T - t0;
+    const int Tc = t1 - t0;
     const float* Sc = S + (size_t)chain * D * D;
     for (int p = threadIdx.x; p < 8 * 4 * 64; p += 256) {
         const int c = p >> 8, kk = (p >> 6) & 3, ln = p & 63;
@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void state_correction_kernel(const float* __re
     __syncthreads();
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, grp = lane >> 4;
     const size_t ts = (size_t)H * D;   // elements per token
-    const float* erow = ell + (size_t)n * Tc * ts + (size_t)h * D;
+    const float* erow = ell + ((size_t)n * (T - e0) + (t0 - e0)) * ts + (size_t)h * D;
     float* orow = o + ((size_t)n * T + t0) * ts + (size_t)h * D;
     for (int step = 0; step < TB / 64; ++step) {
         const int tt = blockIdx.x * TB + 64 * step + 16 * wave;   // first of this wave's 16 tokens
@@ -142,11 +142,11 @@ __global__ __launch_bounds__(256) void state_correction_kernel(const float* __re
 }  // namespace seg
 
 hipError_t launch_state_correction(const float* S, const float* ell, float* o, int B, int T, int H, int t0,
-                                   hipStream_t stream) {
-    const int Tc = T - t0;
+                                   int t1, int e0, hipStream_t stream) {
+    const int Tc = t1 - t0;
     if (B <= 0 || H <= 0 || Tc <= 0) return hipSuccess;
     hipLaunchKernelGGL(seg::state_correction_kernel, dim3((Tc + seg::TB - 1) / seg::TB, B * H), dim3(256), 0, stream,
-                       S, ell, o, T, H, t0);
+                       S, ell, o, T, H, t0, t1, e0);
     return hipGetLastError();
 }
 

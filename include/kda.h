@@ -128,11 +128,16 @@ kda_status_t kda_fwd_check(const void* q, const void* k, const void* v, const fl
  * Pmap S_start + R; o = o from zero + S_start^T ell, with ell the slice's
  * output from the identity with v = 0), so later slices are run from zero and
  * from the identity alongside the first. Two routes:
- *  - two slices: with desc->workspace of at least kda_fwd_workspace_size(desc)
- *    bytes (three fp32 states per (sequence, head) and ell, fp32
- *    [B, T - T2, H, 128], where T2 = T/2 rounded down to a multiple of 32): one
- *    pass over half the length, then hT = Pmap S1 + R and the second half's o
- *    corrected by S1^T ell;
+ *  - one pass: with desc->workspace of at least kda_fwd_workspace_size(desc)
+ *    bytes, 16-byte aligned. S slices, S the largest number (at most 4, each
+ *    at least 4096 tokens) for which the 2S - 1 runs of every (sequence, head)
+ *    fit on the device's compute units at one workgroup each; slice j starts
+ *    at token j T / S rounded down to a multiple of 32. One launch runs them
+ *    all (its end states and ell into the workspace), then S_{j+1} =
+ *    Pmap_j S_j + R_j in turn (the last is hT) and each later slice's o is
+ *    corrected by S_j^T ell. Workspace: three fp32 states per (sequence, head)
+ *    and later slice, and ell, fp32 [B, T - T1, H, 128] with T1 the first
+ *    token of slice 1;
  *  - three slices: with a smaller workspace of at least 256 KiB per
  *    (sequence, head), or none (then a stream-ordered allocation of that size
  *    on `stream`, freed on the same stream; if that allocation fails, the
@@ -143,12 +148,13 @@ kda_status_t kda_fwd(const void* q, const void* k, const void* v, const float* g
                      void* o, float* hT, const kda_desc_t* desc, void* stream);
 
 /* Bytes of device workspace kda_fwd (and kda_gdn_fwd) takes for this
- * descriptor on the current device with its two-slice route for few long
+ * descriptor on the current device with its one-pass slice route for few long
  * chains (bf16, T >= 12288, at most one chain per six compute units of the
- * current device, no cu_seqlens): 196,608 per (sequence, head) plus
- * 512 * B * (T - T2) * H with T2 = T/2 rounded down to a multiple of 32;
- * else 0. A workspace of 262,144 per (sequence, head) up to this size runs the
- * three-slice route without allocating.
+ * current device, no cu_seqlens): 196,608 per (sequence, head) and later
+ * slice plus 512 * B * (T - T1) * H, with the slice count and T1 as described
+ * at kda_fwd (T = 131072, H = 32 on 256 compute units: four slices, 18 MiB +
+ * 1.5 GiB); else 0. A workspace of 262,144 per (sequence, head) up to this
+ * size runs the three-slice route without allocating.
  * The descriptor does not say whether cu_seqlens will be passed; with B ==
  * num_seqs == 1 the fixed-length answer is returned, which is never smaller
  * than what a varlen call needs. 0 also for an invalid descriptor. Host only;
@@ -161,7 +167,7 @@ size_t kda_fwd_workspace_size(const kda_desc_t* desc);
  * layouts, results and errors as kda_fwd; desc->workspace is ignored. The
  * slice routes' workspace comes from a static device array of
  * kda_fwd_noalloc_max_workspace() bytes (8 MiB) that each GPU holds from the
- * first call on it until the process ends: the two-slice route when
+ * first call on it until the process ends: the one-pass slice route when
  * kda_fwd_workspace_size(desc) fits there, else the three-slice route (256 KiB
  * per sequence-head: up to 32). A descriptor whose three-slice workspace does
  * not fit either returns KDA_ERR_WORKSPACE before anything is enqueued. No

@@ -70,7 +70,7 @@ int main() {
     d = desc(1, 8192, 96);
     EXPECT(kda_fwd_workspace_size(&d) == 0);
     d = desc(1, 131072, 32);
-    EXPECT(kda_fwd_workspace_size(&d) == ((size_t)6 << 20) + ((size_t)1 << 30));   // two-slice route
+    EXPECT(kda_fwd_workspace_size(&d) == ((size_t)18 << 20) + ((size_t)3 << 29));   // one pass, four slices
 
     // a valid call launches (stubbed) kernels with consistent arguments
     kda::g_calls.clear();
@@ -79,25 +79,32 @@ int main() {
     EXPECT(kda::g_calls.size() == 1 && strcmp(kda::g_calls[0].what, "pipe") == 0);
     EXPECT(kda::g_calls[0].args.nchains == 96 && kda::g_calls[0].args.ntasks == 0);
 
-    // the two-slice route with a caller workspace of kda_fwd_workspace_size:
-    // one pass (three tasks, the identity task's o into the workspace after
-    // three states per chain), the combine into hT, the output correction
+    // the one-pass route with a caller workspace of kda_fwd_workspace_size: four
+    // slices of 32768 tokens in one launch (seven tasks: slice 0 for real, then
+    // each later slice from zero and from the identity, the identity runs' o
+    // into the workspace after nine states per chain), the combines into S2,
+    // S3 and hT, one output correction per later slice
     static float ws_stand_in[4];
     kda::g_calls.clear();
     d = desc(1, 131072, 32);
     d.workspace = ws_stand_in;
     d.workspace_bytes = kda_fwd_workspace_size(&d);
     EXPECT(kda_fwd(P, P, P, F, F, nullptr, F, F, F, &d, nullptr) == KDA_OK);
-    EXPECT(kda::g_calls.size() == 3);
-    if (kda::g_calls.size() == 3) {
+    EXPECT(kda::g_calls.size() == 7);
+    if (kda::g_calls.size() == 7) {
         const kda::FwdArgs& p = kda::g_calls[0].args;
-        EXPECT(strcmp(kda::g_calls[1].what, "affine_combine") == 0);
-        EXPECT(strcmp(kda::g_calls[2].what, "state_correction") == 0);
-        EXPECT(p.ntasks == 3 && p.nchains == 96);
-        EXPECT(p.task[0].t_begin == 0 && p.task[0].t_end == 65536 && p.task[0].o == nullptr);
-        EXPECT(p.task[1].t_begin == 65536 && p.task[1].t_end == 131072 && p.task[1].o == nullptr);
-        EXPECT(p.task[2].o == ws_stand_in + 3 * 32 * 128 * 128 && p.task[2].o_t0 == 65536 &&
-               p.task[2].o_T == 65536 && p.task[2].flags == (kda::TASK_ZERO_V | kda::TASK_IDENTITY_H0));
+        for (int c = 1; c <= 3; ++c) EXPECT(strcmp(kda::g_calls[c].what, "affine_combine") == 0);
+        for (int c = 4; c <= 6; ++c) EXPECT(strcmp(kda::g_calls[c].what, "state_correction") == 0);
+        EXPECT(p.ntasks == 7 && p.nchains == 7 * 32);
+        EXPECT(p.task[0].t_begin == 0 && p.task[0].t_end == 32768 && p.task[0].o == nullptr);
+        for (int j = 1; j < 4; ++j) {
+            const kda::FwdTask& z = p.task[2 * j - 1];
+            const kda::FwdTask& e = p.task[2 * j];
+            EXPECT(z.t_begin == 32768 * j && z.t_end == 32768 * (j + 1) && z.o == nullptr && z.flags == 0);
+            EXPECT(e.t_begin == 32768 * j && e.t_end == 32768 * (j + 1));
+            EXPECT(e.o == ws_stand_in + 9 * 32 * 128 * 128 && e.o_t0 == 32768 && e.o_T == 98304 &&
+                   e.flags == (kda::TASK_ZERO_V | kda::TASK_IDENTITY_H0));
+        }
     }
 
     // the three-slice route with a smaller caller workspace (four states per

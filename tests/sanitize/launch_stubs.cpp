@@ -19,7 +19,7 @@ hipError_t launch_affine_combine(const float*, const float*, const float*, float
     rec("affine_combine", nullptr);
     return hipSuccess;
 }
-hipError_t launch_state_correction(const float*, const float*, float*, int, int, int, int, hipStream_t) {
+hipError_t launch_state_correction(const float*, const float*, float*, int, int, int, int, int, int, hipStream_t) {
     rec("state_correction", nullptr);
     return hipSuccess;
 }

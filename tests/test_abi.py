@@ -129,19 +129,28 @@ def test_staged_layout(K):
 
 def test_fwd_workspace_size(K):
     """kda_fwd_workspace_size reports what kda_fwd itself uses: nothing for the
-    single fused launch; for few long chains the two-slice route's three 64 KiB
-    fp32 states per (sequence, head) and its fp32 ell for the second half
-    [B, T - T/2, H, 128] (this machine has no GPU, so the library assumes the
-    MI355X's 256 compute units)."""
+    single fused launch; for few long chains the one-pass slice route's three
+    64 KiB fp32 states per (sequence, head) and later slice and its fp32 ell for
+    every slice after the first [B, T - (first token of slice 1), H, 128]. The
+    slice count S is the largest that puts all 2S - 1 runs of every chain on the
+    chip at once (one workgroup each), at most 4 and at most T / 4096 (this
+    machine has no GPU, so the library assumes the MI355X's 256 compute
+    units)."""
     size = lambda d: K.lib().kda_fwd_workspace_size(ctypes.byref(d))
-    two = lambda B, T, H: B * H * 3 * 128 * 128 * 4 + B * (T - (T // 2) // 32 * 32) * H * 128 * 4
+
+    def one_pass(B, T, H):
+        S = max(2, min(4, (256 // (B * H) + 1) // 2, T // 4096))
+        b1 = (T // S) // 32 * 32
+        return B * H * 3 * (S - 1) * 128 * 128 * 4 + B * (T - b1) * H * 128 * 4
     assert size(desc(K, T=8192, H=96)) == 0                          # headline shape: one fused launch
     assert size(desc(K, T=8192, H=64)) == 0
     assert size(desc(K, T=8192, N=6, H=96)) == 0                     # varlen: never sliced
-    assert size(desc(K, T=131072, H=32)) == two(1, 131072, 32)        # 6 MiB + 1 GiB
-    assert size(desc(K, T=131072, H=32)) == (6 << 20) + (1 << 30)
-    assert size(desc(K, T=65536, H=32)) == two(1, 65536, 32)          # each half of the 2 x 65536 handoff
-    assert size(desc(K, T=12301, B=2, H=3)) == two(2, 12301, 3)       # second slice from token 6144
+    assert size(desc(K, T=131072, H=32)) == one_pass(1, 131072, 32)   # four slices: 18 MiB + 1.5 GiB
+    assert size(desc(K, T=131072, H=32)) == (18 << 20) + (3 << 29)
+    assert size(desc(K, T=65536, H=32)) == one_pass(1, 65536, 32)     # each half of the 2 x 65536 handoff
+    assert size(desc(K, T=12301, B=2, H=3)) == one_pass(2, 12301, 3)  # three slices, from tokens 4096 and 8192
+    assert size(desc(K, T=12301, B=2, H=3)) == 6 * 3 * 2 * 65536 + 2 * (12301 - 4096) * 3 * 512
+    assert size(desc(K, T=131072, H=42)) == one_pass(1, 131072, 42)   # 42 chains: three slices
     assert size(desc(K, T=12287, H=32)) == 0                         # too short to slice
     assert size(desc(K, T=131072, H=48)) == 0                        # more than one chain per six CUs
     assert size(desc(K, T=131072, H=32, in_dt=1)) == 0               # fp32 inputs run whole

@@ -5,8 +5,9 @@ state. Both the pages' gate draw and a mild gate (g x 0.01, memory of about
 120 tokens) are run: with the pages' draw the state forgets within about 20
 tokens, so only the mild gate makes h0, the handover and the slice routes'
 affine combines (three slices: starting at tokens 43680 and 87360, or 21824
-and 43680 within each half; two slices: the second from token 65536, its
-outputs corrected by S1^T ell) matter at full length."""
+and 43680 within each half; one pass: four slices starting at tokens 32768,
+65536 and 98304, or 16384, 32768 and 49152 within each half, their outputs
+corrected by S_j^T ell) matter at full length."""
 import numpy as np
 import pytest
 
@@ -42,12 +43,13 @@ def case(gate):
 
 
 def fwd(t, route="three"):
-    """route "three": no workspace (the three-slice route); "two": a workspace of
-    fwd_workspace_size bytes (the two-slice route and its output correction)."""
+    """route "three": no workspace (the three-slice route); "one_pass": a
+    workspace of fwd_workspace_size bytes (every slice in one launch, then the
+    combines and the output corrections)."""
     import torch
     import gated_delta_rule_63_amd as kda
     ws = None
-    if route == "two":
+    if route == "one_pass":
         ws = torch.empty(kda.fwd_workspace_size(t["q"]), dtype=torch.uint8, device=t["q"].device)
     o, hT = kda.fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], initial_state=t["h0"], workspace=ws)
     torch.cuda.synchronize()
@@ -60,7 +62,7 @@ def halves(t):
     return first, second
 
 
-@pytest.mark.parametrize("route", ["two", "three"])
+@pytest.mark.parametrize("route", ["one_pass", "three"])
 @pytest.mark.parametrize("gate", ["bj", "mild"])
 def test_long_context_all_heads(gate, route):
     inp, ro, rs = case(gate)

@@ -2,8 +2,9 @@
 when the chains are few and long (bf16, fixed length, T >= 12288 and at most
 one sixth as many chains as compute units). A slice's state map is affine,
 S_end = Pmap S_start + R, and so are its outputs. With a workspace of
-fwd_workspace_size bytes kda_fwd takes the two-slice route (one pass, then the
-output correction S1^T ell); without one, the three-slice route (two passes).
+fwd_workspace_size bytes kda_fwd takes the one-pass route (every slice in one
+launch, one workgroup per run, then the output corrections S_j^T ell); without
+one, the three-slice route (two passes).
 These tests run both routes against the fp64 oracle."""
 import numpy as np
 import pytest
@@ -21,14 +22,14 @@ def _gpu():
         pytest.skip("no GPU")
 
 
-ROUTES = ["two", "three"]
+ROUTES = ["one_pass", "three"]
 
 
 def fwd(t, route, final_state=None, gdn=None):
     import torch
     import gated_delta_rule_63_amd as kda
     ws = None
-    if route == "two":
+    if route == "one_pass":
         n = kda.fwd_workspace_size(t["q"])
         assert n > 0
         ws = torch.empty(n, dtype=torch.uint8, device=t["q"].device)
@@ -102,12 +103,12 @@ def test_sliced_chain_scalar_gate(route):
     assert eo <= tol_o and es <= tol_s
 
 
-def test_two_slice_route_without_final_state():
-    """The two-slice route with no final state requested: the combine is skipped,
-    the output correction still runs."""
+def test_one_pass_route_without_final_state():
+    """The one-pass slice route with no final state requested: the last combine
+    is skipped, the other combines and the output corrections still run."""
     import torch
     import gated_delta_rule_63_amd as kda
-    cfg = W.variant("T131072_H32", T=12352, H=2, gate="mild", h0=True, name="two slices, no hT")
+    cfg = W.variant("T131072_H32", T=12352, H=2, gate="mild", h0=True, name="one pass, no hT")
     inp = W.make_inputs(cfg, 14)
     t = to_device(inp, "bf16")
     ws = torch.empty(kda.fwd_workspace_size(t["q"]), dtype=torch.uint8, device=t["q"].device)
@@ -117,5 +118,5 @@ def test_two_slice_route_without_final_state():
     assert hT is None
     ro, _ = run_oracle(inp)
     eo = rel_err(o.cpu().numpy(), ro)
-    log(f"[slices] two, no hT, T=12352 H=2: err_o {eo:.2e}")
+    log(f"[slices] one pass, no hT, T=12352 H=2: err_o {eo:.2e}")
     assert eo <= TOL["bf16"][0]
