@@ -23,7 +23,7 @@ def test_noalloc_rejects_oversized_workspace():
     P = ctypes.c_void_p(0x1000)
     # 40 chains on the slice routes: the one-pass route (what kda_fwd_workspace_size
     # reports; three slices here) takes 3 states per chain and later slice and
-    # ell for the last two slices, the three-slice route 4 states per chain
+    # ell for slices 1 and 2, the three-slice route 4 states per chain
     # (10 MiB): both exceed the 8 MiB array
     d = kda.Desc(1, 12288, 40, 128, 128, 1, 0, 1, None, 0)
     assert L.kda_fwd_workspace_size(ctypes.byref(d)) == 40 * 3 * 2 * 128 * 128 * 4 + 8192 * 40 * 128 * 4
