@@ -131,6 +131,7 @@ size_t slice_workspace_bytes(long long nchains) { return (size_t)nchains * 4 * 1
 // chip at once; each slice keeps at least kMinSlice tokens. At least 2.
 constexpr int kMaxSlices = (kda::kMaxTasks + 1) / 2;
 int multi_slice_count(long long nchains, int T, int cus) {
+    if (nchains <= 0) return 2;
     long long n = (cus / nchains + 1) / 2;
     n = std::min<long long>(n, kMaxSlices);
     n = std::min<long long>(n, T / kMinSlice);
