@@ -101,46 +101,53 @@ struct Offs {
     uint32_t v;    // (tid >> 3) * ts + vcol0 + (tid & 7) * 8 : V tile slice
 };
 
+// Rows past the chunk's valid rows (nv >= 1) load the last valid row instead
+// and are then replaced by zeros: every load is in bounds and unconditional,
+// so the fetched values stay in registers.
 template <bool F32>
 __device__ __forceinline__ void fetch(Fetch<F32>& f, const FwdArgs& a, long long cbase, long long cbeta,
                                       uint32_t ts, const Offs& of, int nv, int qq, int tid) {
-    const float* gch = a.g + cbase;
+    const long long gk0 = cbase + (long long)of.gk - (long long)(8 * qq) * ts;   // row 0, channels 2cp, 2cp+1
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
         const int rr = 8 * qq + t;
-        const uint32_t o = of.gk + (uint32_t)t * ts;
-        if (rr < nv) {
-            if (a.scalar_gate) {
-                const float gs = a.g[cbeta + (uint32_t)rr * (uint32_t)a.H];
-                f.g[t] = make_float2(gs, gs);
-            } else {
-                f.g[t] = *reinterpret_cast<const float2*>(gch + o);
-            }
-            if constexpr (F32) {
-                f.k[t] = *reinterpret_cast<const float2*>(static_cast<const float*>(a.k) + cbase + o);
-                f.q[t] = *reinterpret_cast<const float2*>(static_cast<const float*>(a.q) + cbase + o);
-            } else {
-                f.k[t] = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.k) + cbase + o);
-                f.q[t] = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.q) + cbase + o);
-            }
+        const bool ok = rr < nv;
+        const int rc = ok ? rr : nv - 1;
+        const long long o = gk0 + (long long)rc * ts;
+        float2 g;
+        if (a.scalar_gate) {
+            const float gs = a.g[cbeta + (long long)rc * a.H];
+            g = make_float2(gs, gs);
         } else {
-            f.g[t] = make_float2(0.f, 0.f);
-            if constexpr (F32) { f.k[t] = make_float2(0.f, 0.f); f.q[t] = make_float2(0.f, 0.f); }
-            else { f.k[t] = 0u; f.q[t] = 0u; }
+            g = *reinterpret_cast<const float2*>(a.g + o);
+        }
+        f.g[t] = ok ? g : make_float2(0.f, 0.f);
+        if constexpr (F32) {
+            const float2 k = *reinterpret_cast<const float2*>(static_cast<const float*>(a.k) + o);
+            const float2 q = *reinterpret_cast<const float2*>(static_cast<const float*>(a.q) + o);
+            f.k[t] = ok ? k : make_float2(0.f, 0.f);
+            f.q[t] = ok ? q : make_float2(0.f, 0.f);
+        } else {
+            const uint32_t k = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.k) + o);
+            const uint32_t q = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.q) + o);
+            f.k[t] = ok ? k : 0u;
+            f.q[t] = ok ? q : 0u;
         }
     }
-    f.beta = (tid < nv) ? a.beta[cbeta + (uint32_t)tid * (uint32_t)a.H] : 0.f;
-    if ((tid >> 3) < nv) {
-        if constexpr (F32) {
-            const float* vp = static_cast<const float*>(a.v) + cbase + of.v;
-            f.v0 = *reinterpret_cast<const float4*>(vp);
-            f.v1 = *reinterpret_cast<const float4*>(vp + 4);
-        } else {
-            f.v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v) + cbase + of.v);
-        }
+    const float b = a.beta[cbeta + (long long)min(tid, nv - 1) * a.H];
+    f.beta = tid < nv ? b : 0.f;
+    const int vr = tid >> 3;
+    const bool vok = vr < nv;
+    const long long vo = cbase + (long long)of.v - (long long)vr * ts + (long long)(vok ? vr : nv - 1) * ts;
+    if constexpr (F32) {
+        const float* vp = static_cast<const float*>(a.v) + vo;
+        const float4 v0 = *reinterpret_cast<const float4*>(vp), v1 = *reinterpret_cast<const float4*>(vp + 4);
+        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+        f.v0 = vok ? v0 : z;
+        f.v1 = vok ? v1 : z;
     } else {
-        if constexpr (F32) { f.v0 = make_float4(0.f, 0.f, 0.f, 0.f); f.v1 = f.v0; }
-        else f.v = make_uint4(0u, 0u, 0u, 0u);
+        const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v) + vo);
+        f.v = vok ? v : make_uint4(0u, 0u, 0u, 0u);
     }
 }
 
