@@ -101,53 +101,53 @@ struct Offs {
     uint32_t v;    // (tid >> 3) * ts + vcol0 + (tid & 7) * 8 : V tile slice
 };
 
-// Rows past the chunk's valid rows (nv >= 1) load the last valid row instead
-// and are then replaced by zeros: every load is in bounds and unconditional,
-// so the fetched values stay in registers.
+// Raw buffer access to the rows of one chunk of a [row][...] tensor: the
+// resource starts at the chunk's first element for this head and ends after
+// the last valid row's `valid_elems` elements, so reads of rows past the end
+// return zero. Word 3 is the gfx9 raw-buffer format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* p, long long elem_off, int elem_bytes, int nv,
+                                                            uint32_t row_elems, int valid_elems) {
+    const char* base = static_cast<const char*>(p) + elem_off * elem_bytes;
+    const int nbytes = nv > 0 ? ((nv - 1) * (int)row_elems + valid_elems) * elem_bytes : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, nbytes, 0x00020000);
+}
+
+// Rows past the chunk's valid rows read as zero through bounded buffer
+// resources: the loads need no branch and no select, so they stay in flight
+// until the next chunk consumes them, and the fetched values stay in registers.
 template <bool F32>
 __device__ __forceinline__ void fetch(Fetch<F32>& f, const FwdArgs& a, long long cbase, long long cbeta,
                                       uint32_t ts, const Offs& of, int nv, int qq, int tid) {
-    const long long gk0 = cbase + (long long)of.gk - (long long)(8 * qq) * ts;   // row 0, channels 2cp, 2cp+1
+    constexpr int EB = F32 ? 4 : 2;   // bytes per q, k, v element
+    const auto rk = rows_rsrc(a.k, cbase, EB, nv, ts, D);
+    const auto rq = rows_rsrc(a.q, cbase, EB, nv, ts, D);
+    const auto rg = a.scalar_gate ? rows_rsrc(a.g, cbeta, 4, nv, (uint32_t)a.H, 1) : rows_rsrc(a.g, cbase, 4, nv, ts, D);
+    const auto rb = rows_rsrc(a.beta, cbeta, 4, nv, (uint32_t)a.H, 1);
+    const auto rv = rows_rsrc(a.v, cbase, EB, nv, ts, D);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-        const int rr = 8 * qq + t;
-        const bool ok = rr < nv;
-        const int rc = ok ? rr : nv - 1;
-        const long long o = gk0 + (long long)rc * ts;
-        float2 g;
+        const uint32_t o = of.gk + (uint32_t)t * ts;   // element offset of (token 8qq + t, channel 2cp)
         if (a.scalar_gate) {
-            const float gs = a.g[cbeta + (long long)rc * a.H];
-            g = make_float2(gs, gs);
+            const float gs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                       rg, (uint32_t)(8 * qq + t) * (uint32_t)a.H * 4u, 0, 0));
+            f.g[t] = make_float2(gs, gs);
         } else {
-            g = *reinterpret_cast<const float2*>(a.g + o);
+            f.g[t] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rg, 4u * o, 0, 0));
         }
-        f.g[t] = ok ? g : make_float2(0.f, 0.f);
         if constexpr (F32) {
-            const float2 k = *reinterpret_cast<const float2*>(static_cast<const float*>(a.k) + o);
-            const float2 q = *reinterpret_cast<const float2*>(static_cast<const float*>(a.q) + o);
-            f.k[t] = ok ? k : make_float2(0.f, 0.f);
-            f.q[t] = ok ? q : make_float2(0.f, 0.f);
+            f.k[t] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rk, 4u * o, 0, 0));
+            f.q[t] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rq, 4u * o, 0, 0));
         } else {
-            const uint32_t k = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.k) + o);
-            const uint32_t q = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.q) + o);
-            f.k[t] = ok ? k : 0u;
-            f.q[t] = ok ? q : 0u;
+            f.k[t] = __builtin_amdgcn_raw_buffer_load_b32(rk, 2u * o, 0, 0);
+            f.q[t] = __builtin_amdgcn_raw_buffer_load_b32(rq, 2u * o, 0, 0);
         }
     }
-    const float b = a.beta[cbeta + (long long)min(tid, nv - 1) * a.H];
-    f.beta = tid < nv ? b : 0.f;
-    const int vr = tid >> 3;
-    const bool vok = vr < nv;
-    const long long vo = cbase + (long long)of.v - (long long)vr * ts + (long long)(vok ? vr : nv - 1) * ts;
+    f.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, (uint32_t)tid * (uint32_t)a.H * 4u, 0, 0));
     if constexpr (F32) {
-        const float* vp = static_cast<const float*>(a.v) + vo;
-        const float4 v0 = *reinterpret_cast<const float4*>(vp), v1 = *reinterpret_cast<const float4*>(vp + 4);
-        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-        f.v0 = vok ? v0 : z;
-        f.v1 = vok ? v1 : z;
+        f.v0 = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rv, 4u * of.v, 0, 0));
+        f.v1 = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rv, 4u * (of.v + 4), 0, 0));
     } else {
-        const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v) + vo);
-        f.v = vok ? v : make_uint4(0u, 0u, 0u, 0u);
+        f.v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, 2u * of.v, 0, 0));
     }
 }
 
